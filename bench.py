@@ -1,0 +1,243 @@
+"""Benchmark of the HARP apply path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--blk f32|bf16|i8]
+
+A step is one pass of the hot path over one batch: for the default workload
+(cayley4096_bf16: 16384 rows x 4096, bf16 rows, schedule (8,8,8,8), Cayley
+blocks over Sylvester H8) one harp_apply launch over the whole batch, inputs
+resident in HBM.  Block materialisation (theta -> blocks, on the GPU) is setup
+and is not timed.  Prints one JSON line.
+
+value = rows/s of the whole job (K steps timed back to back, bracketed by
+device synchronisation).  roofline.achieved = algorithmic bytes per launch
+(rows * d * 2 bytes read + rows * d * 2 bytes written) / the kernel's mean
+duration, measured with HIP events recorded on the stream the kernel runs on.
+cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["structured_rotations_amd/csrc/" + f for f in
+                  ("apply_tile.hip", "tile_io.h", "common.h", "rht.hip", "rotate_cols.hip")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        p = os.path.join(ROOT, f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, blk: str):
+    """Counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled
+    by a copy-kernel calibration), if a profile taken with the current kernel
+    sources is committed; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_{blk}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w: dict, blk: str, budget_s: float = 30.0) -> dict:
+    """Time the oracle (as it stands) single-threaded on a bounded sample."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import harp_oracle as O
+    kind = w["workload"].kind
+    with threadpool_limits(1):
+        if kind == "rht":
+            x = w["x"].astype(np.float64)
+            n = x.shape[0]
+            chunk = 1024
+            t0 = time.perf_counter()
+            done = 0
+            while done < n and time.perf_counter() - t0 < budget_s:
+                O.rht_compose(x[done:done + chunk], w["signs"].astype(float))
+                done += min(chunk, n - done)
+            dt = time.perf_counter() - t0
+            return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                    "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread"}
+        if kind == "two_sided":
+            t0 = time.perf_counter()
+            bu = O.stored_blocks(O.materialize_blocks(w["su"], w["d_out"], w["theta_u"], w["gauss_u"]), blk)
+            bv = O.stored_blocks(O.materialize_blocks(w["schedule"], w["d"], w["theta_v"], w["gauss_v"]), blk)
+            t1 = time.perf_counter()
+            O.rotate_weight(w["x"].astype(np.float64), w["su"], bu, w["signs_u"].astype(float), w["schedule"], bv,
+                            w["signs_v"].astype(float))
+            dt = time.perf_counter() - t1
+            return {"value": 1.0 / dt, "unit": "weights/s", "cores": 1, "kind": "oracle",
+                    "sample": f"the full {w['d_out']}x{w['d']} weight, fp64 numpy, 1 thread "
+                              f"(block setup {t1 - t0:.1f}s not counted)"}
+        blocks = O.stored_blocks(O.materialize_blocks(w["schedule"], w["d"], w["theta"], w["gauss"]), blk)
+        x = w["x"]
+        n = x.shape[0]
+        chunk = 2048
+        t0 = time.perf_counter()
+        done = 0
+        while done < n and time.perf_counter() - t0 < budget_s:
+            O.apply(x[done:done + chunk].astype(np.float64), w["schedule"], blocks, w["signs"].astype(float))
+            done += min(chunk, n - done)
+        dt = time.perf_counter() - t0
+        return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cayley4096_bf16")
+    ap.add_argument("--blk", default="f32", choices=["f32", "bf16", "i8"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device copy of the batch instead (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the apply path has no cross-GPU step and this build runs on a "
+              "single MI355X; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from structured_rotations_amd import api
+    from structured_rotations_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.make(args.workload)
+    wl = w["workload"]
+    d, sch, io = w["d"], w["schedule"], w["io"]
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    eb = 2 if io == "bf16" else 4
+    x = torch.from_numpy(w["x"]).to(tdt).cuda()
+    rows = x.shape[0]
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        def step():
+            y.copy_(x)
+        alg_bytes = rows * d * eb * 2
+        units = rows
+    elif wl.kind == "rht":
+        sg = torch.from_numpy(w["signs"]).cuda()
+
+        def step():
+            api.rht_compose(sch, d, sg, x, y)
+        alg_bytes = rows * d * eb * 2
+        units = rows
+    elif wl.kind == "two_sided":
+        bu, scu = api.harp_materialize_blocks(w["su"], w["d_out"], torch.from_numpy(w["theta_u"]).cuda(),
+                                              torch.from_numpy(w["gauss_u"]).cuda(), args.blk)
+        bv, scv = api.harp_materialize_blocks(sch, d, torch.from_numpy(w["theta_v"]).cuda(),
+                                              torch.from_numpy(w["gauss_v"]).cuda(), args.blk)
+        su_s = torch.from_numpy(w["signs_u"]).cuda()
+        sv_s = torch.from_numpy(w["signs_v"]).cuda()
+
+        def step():
+            api.harp_rotate_weight(w["su"], bu, scu, su_s, sch, bv, scv, sv_s, x, y)
+        alg_bytes = rows * d * eb * 2
+        units = 1
+    else:
+        th = torch.from_numpy(w["theta"]).cuda()
+        gs = torch.from_numpy(w["gauss"]).cuda() if w["gauss"].size else None
+        blocks, scales = api.harp_materialize_blocks(sch, d, th, gs, args.blk)
+        sg = torch.from_numpy(w["signs"]).cuda()
+
+        def step():
+            api.harp_apply(sch, d, blocks, scales, sg, x, y)
+        alg_bytes = rows * d * eb * 2
+        units = rows
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+    kern_ms = float(per_launch.mean())
+    value = units / (ms_per_step * 1e-3)
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    # spot parity check of the benchmarked output against the oracle (8 rows)
+    parity = None
+    if not args.copy_calibration and wl.kind == "apply":
+        from oracle import harp_oracle as O
+        idx = np.array([0, rows // 3, rows // 2, rows - 1])
+        ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
+        ref = O.apply(w["x"][idx].astype(np.float64), sch, ob, w["signs"].astype(float))
+        got = y[torch.from_numpy(idx).cuda()].float().cpu().numpy()
+        parity = float(O.row_rel_l2(got, ref).max())
+
+    unit = {"apply": "rows/s", "rht": "rows/s", "two_sided": "weights/s"}[wl.kind]
+    traffic = None if args.copy_calibration else traffic_from_profile(args.workload, args.blk)
+    line = {
+        "metric": "HARP apply rows/s + achieved HBM GB/s (% of peak), d=4096/5120 bf16",
+        "value": round(value, 1),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-io/f32-compute" if io == "bf16" else "f32",
+        "data": "synthetic (seeded Student-t nu=3 rows with outlier channels; random Cayley/Givens parameters)",
+        "config": {"workload": args.workload if not args.copy_calibration else "device copy of " + args.workload,
+                   "rows": rows, "d": d, "schedule": list(sch), "io": io, "blocks": args.blk,
+                   "kind": wl.kind, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "kernel_ms_mean": round(kern_ms, 5),
+        "kernel_ms_p10_p90": [round(float(np.percentile(per_launch, 10)), 5),
+                              round(float(np.percentile(per_launch, 90)), 5)],
+        "alg_bytes_per_launch": alg_bytes,
+        "wall_s_timed": round(wall, 4),
+        "parity_max_row_rel_l2": parity,
+    }
+    if not args.no_cpu_baseline and not args.copy_calibration:
+        line["cpu_baseline"] = cpu_baseline(w, args.blk)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,43 @@
+// Launchers for the gfx950 kernels (host side, called by the C ABI layer
+// after every argument has been validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace harp {
+
+enum class DT : int { F32 = 0, BF16 = 1, I8 = 2, F64 = 3 };
+
+// Element size in bytes of an I/O dtype (F32 or BF16).
+inline int io_bytes(DT t) { return t == DT::F32 ? 4 : 2; }
+
+// Rows of length pl.d:  y = M x  (inverse=false) or  y = M^T x  (inverse=true).
+// sign_mode: 0 = no sign, 1 = sign on the input side (forward), 2 = sign on the
+// output side (inverse).  stage_lo/stage_hi restrict the stages applied
+// (all stages: 0, pl.m).
+hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, DT bdt,
+                             const float* scales, const int8_t* signs, const void* x,
+                             int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
+                             int64_t rows, hipStream_t stream);
+
+// Column passes of the two-sided rotation: apply stages [t0, t1) of the
+// schedule `pl` (acting on the row index of a pl.d x ncols matrix) to every
+// column.  Forward order (inverse=false) or transposed blocks in reverse
+// order (inverse=true).  sign_mode as above (sign indexed by the row).
+hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const void* blocks,
+                             DT bdt, const float* scales, const int8_t* signs, int sign_mode,
+                             const void* x, int64_t ldx, DT in_dt, void* y, int64_t ldy,
+                             DT out_dt, int64_t ncols, hipStream_t stream);
+
+// k composed randomized Hadamard transforms over rows (all radices powers of two).
+hipError_t launch_rht(const Plan& pl, const int8_t* signs, int k, bool inverse, const void* x,
+                      int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt, int64_t rows,
+                      hipStream_t stream);
+
+// B_{t,c} = Q_{t,c}(theta) G_{b_t} for all stages, in fp64, rounded to bdt.
+hipError_t launch_materialize(const Plan& pl, const double* theta, const double* gauss, DT bdt,
+                              void* blocks, float* scales, hipStream_t stream);
+
+}  // namespace harp

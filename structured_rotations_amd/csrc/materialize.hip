@@ -1,0 +1,197 @@
+// Block materialisation  B_{t,c} = Q_{t,c}(theta) G_{b_t},  in fp64 on device.
+//
+// HARP technical summary (gist.science 2605.29843), §2.2: every learnable
+// block is a learnable orthogonal factor Q (a Givens rotation for radix 2, a
+// Cayley map for larger radices) times a fixed base mixer G (the normalised
+// Sylvester Hadamard for power-of-two radices, otherwise the Q factor of the
+// QR factorisation of a fixed Gaussian matrix, §2.1).  With all parameters
+// zero, Q = I and the block is G.  §2.4: parameters may be stored in int8;
+// the same idea is offered here for the blocks (one fp32 scale per block).
+//
+// One launch per stage.  Thread 0 of each workgroup builds G in LDS
+// (Householder QR with the column signs fixed so that diag R > 0); every
+// thread then forms one group's Q (Cayley: Gaussian elimination on
+// (I + A) Q = (I - A); no pivoting is needed because I + A has the identity
+// as its symmetric part), multiplies by G and rounds to the storage format.
+#include <cmath>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace harp {
+
+struct MatParams {
+  int64_t ngroups;
+  const double* theta;   // the stage's parameters
+  const double* gauss;   // the stage's b x b Gaussian matrix, or NULL
+  int out_dt;            // 0 F32, 1 BF16, 2 I8
+  void* out;             // the stage's blocks
+  float* scales;         // the stage's int8 scales
+};
+
+template <int B>
+__device__ void base_mixer(const double* gauss, double* g) {
+  if (gauss == nullptr) {
+    const double inv = 1.0 / sqrt((double)B);
+    for (int r = 0; r < B; ++r)
+      for (int k = 0; k < B; ++k) g[r * B + k] = (__popc(r & k) & 1) ? -inv : inv;
+    return;
+  }
+  double a[B][B], q[B][B];
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      a[r][k] = gauss[r * B + k];
+      q[r][k] = (r == k) ? 1.0 : 0.0;
+    }
+  // Householder: a <- H_{B-2} ... H_0 a = R,  q <- q H_0 ... H_{B-2} = Q.
+  for (int k = 0; k < B - 1; ++k) {
+    double nrm = 0.0;
+    for (int i = k; i < B; ++i) nrm += a[i][k] * a[i][k];
+    nrm = sqrt(nrm);
+    if (nrm == 0.0) continue;
+    const double alpha = a[k][k] > 0 ? -nrm : nrm;
+    double v[B];
+    for (int i = 0; i < B; ++i) v[i] = (i < k) ? 0.0 : a[i][k];
+    v[k] -= alpha;
+    double vn = 0.0;
+    for (int i = k; i < B; ++i) vn += v[i] * v[i];
+    if (vn == 0.0) continue;
+    for (int j = 0; j < B; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < B; ++i) dot += v[i] * a[i][j];
+      const double f = 2.0 * dot / vn;
+      for (int i = k; i < B; ++i) a[i][j] -= f * v[i];
+    }
+    for (int r = 0; r < B; ++r) {
+      double dot = 0.0;
+      for (int i = k; i < B; ++i) dot += q[r][i] * v[i];
+      const double f = 2.0 * dot / vn;
+      for (int i = k; i < B; ++i) q[r][i] -= f * v[i];
+    }
+  }
+  for (int k = 0; k < B; ++k) {
+    const double sg = a[k][k] < 0 ? -1.0 : 1.0;
+    for (int r = 0; r < B; ++r) g[r * B + k] = q[r][k] * sg;
+  }
+}
+
+template <int B>
+__global__ void __launch_bounds__(256) materialize_kernel(MatParams p) {
+  __shared__ double g[B * B];
+  if (threadIdx.x == 0) base_mixer<B>(p.gauss, g);
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= p.ngroups) return;
+  double q[B][B];
+  if (B == 2) {
+    const double th = p.theta[c];
+    const double cs = cos(th), sn = sin(th);
+    q[0][0] = cs; q[0][1] = -sn;
+    q[1][0] = sn; q[1][1] = cs;
+  } else {
+    constexpr int per = B * (B - 1) / 2;
+    const double* th = p.theta + c * per;
+    double mtx[B][B];
+    for (int r = 0; r < B; ++r)
+      for (int k = 0; k < B; ++k) { mtx[r][k] = (r == k) ? 1.0 : 0.0; q[r][k] = mtx[r][k]; }
+    int idx = 0;
+    for (int r = 0; r < B; ++r)
+      for (int k = r + 1; k < B; ++k) {
+        const double a = th[idx++];
+        mtx[r][k] += a; mtx[k][r] -= a;   // I + A
+        q[r][k] -= a;   q[k][r] += a;     // I - A
+      }
+    for (int k = 0; k < B; ++k) {
+      const double inv = 1.0 / mtx[k][k];
+      for (int i = k + 1; i < B; ++i) {
+        const double f = mtx[i][k] * inv;
+        if (f == 0.0) continue;
+        for (int j = k; j < B; ++j) mtx[i][j] -= f * mtx[k][j];
+        for (int j = 0; j < B; ++j) q[i][j] -= f * q[k][j];
+      }
+    }
+    for (int k = B - 1; k >= 0; --k) {
+      for (int j = 0; j < B; ++j) {
+        double acc = q[k][j];
+        for (int i = k + 1; i < B; ++i) acc -= mtx[k][i] * q[i][j];
+        q[k][j] = acc / mtx[k][k];
+      }
+    }
+  }
+  double blk[B][B];
+  double amax = 0.0;
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < B; ++i) acc += q[r][i] * g[i * B + k];
+      blk[r][k] = acc;
+      amax = fmax(amax, fabs(acc));
+    }
+  const int64_t o = c * B * B;
+  if (p.out_dt == 0) {
+    float* out = static_cast<float*>(p.out) + o;
+    for (int r = 0; r < B; ++r)
+      for (int k = 0; k < B; ++k) out[r * B + k] = (float)blk[r][k];
+  } else if (p.out_dt == 1) {
+    uint16_t* out = static_cast<uint16_t*>(p.out) + o;
+    for (int r = 0; r < B; ++r)
+      for (int k = 0; k < B; ++k) out[r * B + k] = f64_to_bf16_rne(blk[r][k]);
+  } else {
+    int8_t* out = static_cast<int8_t*>(p.out) + o;
+    const float sc = (float)(amax / 127.0);
+    p.scales[c] = sc;
+    for (int r = 0; r < B; ++r)
+      for (int k = 0; k < B; ++k) {
+        double code = 0.0;
+        if (sc > 0.0f) code = fmin(127.0, fmax(-127.0, rint(blk[r][k] / (double)sc)));
+        out[r * B + k] = (int8_t)code;
+      }
+  }
+}
+
+namespace {
+template <int B>
+hipError_t launch_mat(const MatParams& p, hipStream_t st) {
+  const int threads = 256;
+  const int64_t grid = (p.ngroups + threads - 1) / threads;
+  hipLaunchKernelGGL(materialize_kernel<B>, dim3((unsigned)grid), dim3(threads), 0, st, p);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_materialize(const Plan& pl, const double* theta, const double* gauss, DT bdt,
+                              void* blocks, float* scales, hipStream_t stream) {
+  const int esz = bdt == DT::F32 ? 4 : (bdt == DT::BF16 ? 2 : 1);
+  for (int t = 0; t < pl.m; ++t) {
+    MatParams p{};
+    p.ngroups = pl.d / pl.radix[t];
+    p.theta = theta + pl.theta_off[t];
+    p.gauss = pl.gauss_off[t] >= 0 ? gauss + pl.gauss_off[t] : nullptr;
+    p.out_dt = (int)bdt;
+    p.out = static_cast<char*>(blocks) + pl.blk_off[t] * esz;
+    p.scales = scales ? scales + pl.grp_off[t] : nullptr;
+    hipError_t e = hipSuccess;
+    switch (pl.radix[t]) {
+      case 2: e = launch_mat<2>(p, stream); break;
+      case 3: e = launch_mat<3>(p, stream); break;
+      case 4: e = launch_mat<4>(p, stream); break;
+      case 5: e = launch_mat<5>(p, stream); break;
+      case 6: e = launch_mat<6>(p, stream); break;
+      case 7: e = launch_mat<7>(p, stream); break;
+      case 8: e = launch_mat<8>(p, stream); break;
+      case 9: e = launch_mat<9>(p, stream); break;
+      case 10: e = launch_mat<10>(p, stream); break;
+      case 11: e = launch_mat<11>(p, stream); break;
+      case 12: e = launch_mat<12>(p, stream); break;
+      case 13: e = launch_mat<13>(p, stream); break;
+      case 14: e = launch_mat<14>(p, stream); break;
+      case 15: e = launch_mat<15>(p, stream); break;
+      case 16: e = launch_mat<16>(p, stream); break;
+      default: e = hipErrorInvalidValue; break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace harp

@@ -1,0 +1,151 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load, export every function include/harp.h declares, size
+its parameter arrays like the oracle, and reject malformed calls on the host
+before any HIP call (so these calls are safe without a device).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import harp_oracle as O
+from structured_rotations_amd import _lib
+from structured_rotations_amd._lib import Schedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "harp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:harp_status|int64_t|size_t|const char\*)\s+(\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    for want in ("harp_apply", "harp_apply_inverse", "harp_rotate_weight", "rht_compose",
+                 "harp_materialize_blocks", "harp_status_str", "harp_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in harp.h but not exported"
+
+
+@pytest.mark.parametrize("schedule", [(2,) * 6, (8, 8, 8, 8), (8, 8, 8, 5, 2), (8, 8, 8, 3, 3, 3), (8, 8, 8, 16),
+                                      (3, 5, 7), (16, 2)])
+def test_size_helpers_match_oracle(lib, schedule):
+    d = int(np.prod(schedule))
+    s = ctypes.byref(Schedule.of(schedule))
+    assert lib.harp_theta_count(s, d) == sum(O.theta_counts(schedule, d))
+    assert lib.harp_gauss_count(s, d) == sum(b * b for b in schedule if not O.is_pow2(b))
+    assert lib.harp_block_count(s, d) == sum(d * b for b in schedule)
+    assert lib.harp_group_count(s, d) == sum(d // b for b in schedule)
+
+
+@pytest.mark.parametrize("schedule,d", [((8, 8), 65), ((1, 64), 64), ((17, 2), 34), ((2,) * 17, 2 ** 17),
+                                        ((), 1), ((8, 8, 8, 8, 8, 8), 8 ** 6)])
+def test_size_helpers_reject_bad_schedules(lib, schedule, d):
+    sch = Schedule()
+    sch.m = len(schedule)
+    for i, b in enumerate(schedule[:16]):
+        sch.radix[i] = b
+    assert lib.harp_theta_count(ctypes.byref(sch), d) == -1
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000)
+
+
+def _apply(lib, schedule=(8, 8), d=64, blocks=FAKE, bdt=_lib.HARP_F32, scales=None, signs=None, x=FAKE,
+           ldx=64, y=FAKE2, ldy=64, rows=4, io=_lib.HARP_F32, inverse=False):
+    fn = lib.harp_apply_inverse if inverse else lib.harp_apply
+    return fn(ctypes.byref(Schedule.of(schedule)), d, blocks, bdt, scales, signs, x, ldx, y, ldy, rows, io, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=65), _lib.HARP_ERR_INVALID_ARG),                       # prod != d
+    (dict(schedule=(8, 9), d=72, rows=-1), _lib.HARP_ERR_INVALID_ARG),
+    (dict(ldx=32), _lib.HARP_ERR_INVALID_ARG),                     # ld < d
+    (dict(x=None), _lib.HARP_ERR_INVALID_ARG),                     # NULL with rows > 0
+    (dict(x=ctypes.c_void_p(0x10002)), _lib.HARP_ERR_INVALID_ARG),  # misaligned f32
+    (dict(io=_lib.HARP_I8), _lib.HARP_ERR_UNSUPPORTED),
+    (dict(io=_lib.HARP_F64), _lib.HARP_ERR_UNSUPPORTED),
+    (dict(bdt=_lib.HARP_F64), _lib.HARP_ERR_UNSUPPORTED),
+    (dict(bdt=_lib.HARP_I8), _lib.HARP_ERR_INVALID_ARG),           # int8 blocks without scales
+    (dict(scales=FAKE), _lib.HARP_ERR_INVALID_ARG),                # scales with f32 blocks
+    (dict(blocks=None), _lib.HARP_ERR_INVALID_ARG),
+    (dict(y=ctypes.c_void_p(0x10000 + 64)), _lib.HARP_ERR_INVALID_ARG),  # partial overlap
+    (dict(y=FAKE, ldy=128), _lib.HARP_ERR_INVALID_ARG),           # in place with different ld
+    (dict(inverse=True, d=63), _lib.HARP_ERR_INVALID_ARG),
+])
+def test_apply_rejects_on_host(lib, kw, status):
+    assert _apply(lib, **kw) == status
+    assert lib.harp_last_error().decode() != ""
+
+
+def test_apply_zero_rows_is_a_noop(lib):
+    assert _apply(lib, rows=0, x=None, y=None) == _lib.HARP_OK
+
+
+def test_oversized_schedule_struct_rejected(lib):
+    sch = Schedule()
+    sch.m = 17
+    assert lib.harp_apply(ctypes.byref(sch), 64, FAKE, 0, None, None, FAKE, 64, FAKE2, 64, 1, 0, None) == \
+        _lib.HARP_ERR_INVALID_ARG
+    assert lib.harp_apply(None, 64, FAKE, 0, None, None, FAKE, 64, FAKE2, 64, 1, 0, None) == _lib.HARP_ERR_INVALID_ARG
+
+
+def test_rht_rejects_on_host(lib):
+    s = ctypes.byref(Schedule.of((8, 5)))
+    assert lib.rht_compose(s, 40, FAKE, 3, FAKE, 40, FAKE2, 40, 2, 0, 0, None) == _lib.HARP_ERR_UNSUPPORTED
+    s = ctypes.byref(Schedule.of((8, 8)))
+    assert lib.rht_compose(s, 64, FAKE, 0, FAKE, 64, FAKE2, 64, 2, 0, 0, None) == _lib.HARP_ERR_INVALID_ARG
+    assert lib.rht_compose(s, 64, FAKE, 9, FAKE, 64, FAKE2, 64, 2, 0, 0, None) == _lib.HARP_ERR_INVALID_ARG
+    assert lib.rht_compose(s, 64, None, 3, FAKE, 64, FAKE2, 64, 2, 0, 0, None) == _lib.HARP_ERR_INVALID_ARG
+    assert lib.rht_compose(s, 64, None, 3, None, 64, None, 64, 0, 0, 0, None) == _lib.HARP_OK
+
+
+def test_materialize_rejects_on_host(lib):
+    s = ctypes.byref(Schedule.of((8, 5)))
+    assert lib.harp_materialize_blocks(s, 40, FAKE, None, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert lib.harp_materialize_blocks(s, 40, None, FAKE, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert lib.harp_materialize_blocks(s, 40, FAKE, FAKE, 2, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert lib.harp_materialize_blocks(s, 40, FAKE, FAKE, 3, FAKE2, None, None) == _lib.HARP_ERR_UNSUPPORTED
+
+
+def test_rotate_weight_rejects_on_host(lib):
+    su = ctypes.byref(Schedule.of((8, 3)))
+    sv = ctypes.byref(Schedule.of((8, 5)))
+    args = dict(bu=FAKE, bv=FAKE, w=FAKE, ldw=40, wo=FAKE2, ldo=40, dout=24, din=40, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.harp_rotate_weight(su, a["bu"], None, None, sv, a["bv"], None, None, 0, a["w"], a["ldw"],
+                                      a["wo"], a["ldo"], a["dout"], a["din"], 0, 0, a["ws"], a["wsb"], None)
+    assert call(dout=25) == _lib.HARP_ERR_INVALID_ARG
+    assert call(din=41) == _lib.HARP_ERR_INVALID_ARG
+    assert call(ldw=39) == _lib.HARP_ERR_INVALID_ARG
+    assert call(bu=None) == _lib.HARP_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p(0x40000), wsb=100) == _lib.HARP_ERR_UNSUPPORTED
+    assert lib.harp_rotate_weight_workspace(24, 40) == 24 * 40 * 4
+    assert lib.harp_rotate_weight_workspace(0, 40) == 0
+
+
+def test_status_strings(lib):
+    assert lib.harp_status_str(0) == b"HARP_OK"
+    assert lib.harp_status_str(-1) == b"HARP_ERR_INVALID_ARG"
+    assert lib.harp_status_str(-2) == b"HARP_ERR_UNSUPPORTED"
+    assert lib.harp_status_str(-3) == b"HARP_ERR_LAUNCH"
+    assert lib.harp_version().startswith(b"harp-gfx950")

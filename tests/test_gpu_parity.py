@@ -1,0 +1,282 @@
+"""Parity of the gfx950 HIP path (through the C ABI) with the fp64 oracle.
+
+Every GPU result is compared with the oracle on the same seeded inputs: the
+same bf16/fp32 row bytes widened to fp64, and the oracle's own blocks rounded
+to the same storage format.  Small cases cover several row tiles and a ragged
+tail element by element; the full-size cases run the full batch in the launch
+configuration the benchmark times and compare a seeded sample of rows.
+Bounds: per-row relative l2 <= 1e-5 for fp32 rows, <= 4e-3 for bf16 rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import harp_oracle as O
+from structured_rotations_amd import api
+from structured_rotations_amd import workloads as W
+from tests.parity_util import (TOL, assert_rows_close, from_dev, gpu_blocks, oracle_blocks, signs_dev, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = np.random.default_rng(99)
+
+
+def _case(name, rows=None):
+    print(f"\n[case] {name} rows={rows}", flush=True)
+    return W.make(name, rows)
+
+
+# ------------------------------------------------------------------ materialisation
+MAT_CASES = [("sylvester64_f32", None), ("cayley4096_bf16", None), ("mixed5120_bf16", None),
+             ("two_sided_13824x5120_bf16", "u"), ("two_sided_13824x5120_bf16", "v")]
+
+
+def _mat_inputs(name, side):
+    w = _case(name, rows=1)
+    if side == "u":
+        return w["su"], w["d_out"], w["theta_u"], w["gauss_u"]
+    if side == "v":
+        return w["schedule"], w["d"], w["theta_v"], w["gauss_v"]
+    return w["schedule"], w["d"], w["theta"], w["gauss"]
+
+
+@pytest.mark.parametrize("name,side", MAT_CASES)
+@pytest.mark.parametrize("blk", ["f32", "bf16", "i8"])
+def test_materialize_matches_oracle(name, side, blk):
+    sch, d, theta, gauss = _mat_inputs(name, side)
+    exact = O.materialize_blocks(sch, d, theta, gauss)
+    ex = np.concatenate([b.ravel() for b in exact])
+    blocks, scales = gpu_blocks(api, sch, d, theta, gauss, blk)
+    torch.cuda.synchronize()
+    if blk == "i8":
+        codes_ref, scales_ref = zip(*[O.quantize_i8(b) for b in exact])
+        codes_ref = np.concatenate([c.ravel() for c in codes_ref]).astype(np.int64)
+        scales_ref = np.concatenate(scales_ref).astype(np.float64)
+        sc = scales.cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(sc, scales_ref, rtol=2.0 ** -23, atol=0)
+        codes = blocks.cpu().numpy().astype(np.int64)
+        per = np.repeat(scales_ref, [b * b for b in sch for _ in range(d // b)])
+        frac = np.abs(ex / per - np.floor(ex / per) - 0.5)
+        near_tie = frac < 1e-6
+        assert np.all((codes == codes_ref) | near_tie)
+        return
+    got = from_dev(blocks)
+    ref = np.concatenate([b.ravel() for b in O.stored_blocks(exact, blk)])
+    ulp = 2.0 ** -24 if blk == "f32" else 2.0 ** -9
+    assert np.all(np.abs(got - ex) <= ulp * np.abs(ex) + 1e-14)
+    assert np.mean(got != ref) < 1e-4
+
+
+# ------------------------------------------------------------------ apply / inverse
+APPLY = ["sylvester64_f32", "cayley4096_bf16", "mixed5120_bf16"]
+SMALL_ROWS = {"sylvester64_f32": 256, "cayley4096_bf16": 37, "mixed5120_bf16": 29}
+
+
+def _apply_refs(w, blk, x):
+    blocks = oracle_blocks(w["schedule"], w["d"], w["theta"], w["gauss"], blk)
+    return blocks, O.apply(x, w["schedule"], blocks, w["signs"].astype(float))
+
+
+@pytest.mark.parametrize("name", APPLY)
+@pytest.mark.parametrize("blk", ["f32", "bf16", "i8"])
+def test_apply_and_inverse_small(name, blk):
+    w = _case(name, SMALL_ROWS[name])
+    sch, d, io = w["schedule"], w["d"], w["io"]
+    x = w["x"].astype(np.float64)
+    blocks_g, scales_g = gpu_blocks(api, sch, d, w["theta"], w["gauss"], blk)
+    sg = signs_dev(w["signs"])
+    xd = to_dev(w["x"], io)
+    y = api.harp_apply(sch, d, blocks_g, scales_g, sg, xd)
+    torch.cuda.synchronize()
+    blocks_o, y_ref = _apply_refs(w, blk, x)
+    assert_rows_close(from_dev(y), y_ref, TOL[io], f"{name}/{blk} forward")
+    # inverse of the GPU output, against the oracle inverse of the same bytes
+    yin = from_dev(y)
+    xr = api.harp_apply_inverse(sch, d, blocks_g, scales_g, sg, y)
+    torch.cuda.synchronize()
+    x_ref = O.apply_inverse(yin, sch, blocks_o, w["signs"].astype(float))
+    assert_rows_close(from_dev(xr), x_ref, TOL[io], f"{name}/{blk} inverse")
+
+
+@pytest.mark.parametrize("name", ["cayley4096_bf16", "mixed5120_bf16"])
+def test_apply_full_size_sampled(name):
+    w = _case(name)
+    sch, d, io = w["schedule"], w["d"], w["io"]
+    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    sg = signs_dev(w["signs"])
+    xd = to_dev(w["x"], io)
+    y = api.harp_apply(sch, d, blocks_g, None, sg, xd)
+    xr = api.harp_apply_inverse(sch, d, blocks_g, None, sg, y)
+    torch.cuda.synchronize()
+    n = w["rows"]
+    idx = np.unique(np.concatenate([[0, 1, n - 1], SAMPLE.choice(n, 96, replace=False)]))
+    blocks_o, y_ref = _apply_refs(w, "f32", w["x"][idx].astype(np.float64))
+    y_s = from_dev(y[torch.from_numpy(idx).cuda()])
+    assert_rows_close(y_s, y_ref, TOL[io], f"{name} full forward")
+    x_ref = O.apply_inverse(y_s, sch, blocks_o, w["signs"].astype(float))
+    assert_rows_close(from_dev(xr[torch.from_numpy(idx).cuda()]), x_ref, TOL[io], f"{name} full inverse")
+
+
+def test_roundtrip_fp32_rows_is_identity():
+    w = _case("cayley4096_bf16", 23)
+    sch, d = w["schedule"], w["d"]
+    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    sg = signs_dev(w["signs"])
+    x = to_dev(w["x"], "f32")
+    back = api.harp_apply_inverse(sch, d, blocks_g, None, sg, api.harp_apply(sch, d, blocks_g, None, sg, x))
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(back), w["x"].astype(np.float64), 1e-5, "roundtrip")
+
+
+@pytest.mark.parametrize("rows", [1, 9, 10, 11])
+def test_apply_ragged_tiles_and_in_place(rows):
+    w = _case("cayley4096_bf16", rows)
+    sch, d = w["schedule"], w["d"]
+    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    sg = signs_dev(w["signs"])
+    xd = to_dev(w["x"], "bf16")
+    _, y_ref = _apply_refs(w, "f32", w["x"].astype(np.float64))
+    y = api.harp_apply(sch, d, blocks_g, None, sg, xd.clone())
+    api.harp_apply(sch, d, blocks_g, None, sg, xd, xd)          # in place
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(y), y_ref, TOL["bf16"], "out of place")
+    assert_rows_close(from_dev(xd), y_ref, TOL["bf16"], "in place")
+
+
+def test_apply_strided_rows_and_zero_rows():
+    w = _case("mixed5120_bf16", 13)
+    sch, d = w["schedule"], w["d"]
+    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    sg = signs_dev(w["signs"])
+    big = torch.zeros(13, d + 24, dtype=torch.bfloat16, device="cuda")
+    big[:, :d] = to_dev(w["x"], "bf16")
+    out = torch.full((13, d + 40), 7.0, dtype=torch.bfloat16, device="cuda")
+    api.harp_apply(sch, d, blocks_g, None, sg, big[:, :d], out[:, :d])
+    torch.cuda.synchronize()
+    _, y_ref = _apply_refs(w, "f32", w["x"].astype(np.float64))
+    assert_rows_close(from_dev(out[:, :d]), y_ref, TOL["bf16"], "strided")
+    assert torch.all(out[:, d:] == 7.0)
+    empty = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+    api.harp_apply(sch, d, blocks_g, None, sg, empty, empty.clone())
+
+
+def test_theta_zero_apply_equals_one_rht():
+    # [HARP technical summary §2.2]: at theta = 0 every block is G_b, so with
+    # Sylvester radices HARP is the RHT H_d D_s.
+    sch, d = (8, 8, 8, 16), 8192
+    rng = np.random.default_rng(5)
+    signs = np.where(rng.integers(0, 2, d) == 1, 1, -1).astype(np.int8)
+    x = W.round_io(rng.standard_t(3, size=(12, d)).astype(np.float32), "f32")
+    th = np.zeros(sum(O.theta_counts(sch, d)))
+    blocks_g, _ = gpu_blocks(api, sch, d, th, None, "f32")
+    xd = to_dev(x, "f32")
+    y1 = api.harp_apply(sch, d, blocks_g, None, signs_dev(signs), xd)
+    y2 = api.rht_compose(sch, d, signs_dev(signs[None, :]), xd)
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(y1), from_dev(y2), 1e-5, "harp(theta=0) vs rht")
+    assert_rows_close(from_dev(y2), O.rht_compose(x.astype(float), signs[None, :].astype(float)), 1e-5, "rht")
+
+
+# ------------------------------------------------------------------ rht_compose
+def test_rht_compose_small_and_inverse():
+    w = _case("rht3_8192_bf16", 41)
+    sch, d = w["schedule"], w["d"]
+    sg = signs_dev(w["signs"])
+    xd = to_dev(w["x"], "bf16")
+    y = api.rht_compose(sch, d, sg, xd)
+    torch.cuda.synchronize()
+    y_ref = O.rht_compose(w["x"].astype(np.float64), w["signs"].astype(float))
+    assert_rows_close(from_dev(y), y_ref, TOL["bf16"], "rht forward")
+    yin = from_dev(y)
+    xr = api.rht_compose(sch, d, sg, y, inverse=True)
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(xr), O.rht_compose(yin, w["signs"].astype(float), inverse=True), TOL["bf16"],
+                      "rht inverse")
+
+
+def test_rht_compose_full_size_sampled():
+    w = _case("rht3_8192_bf16")
+    sch, d = w["schedule"], w["d"]
+    sg = signs_dev(w["signs"])
+    xd = to_dev(w["x"], "bf16")
+    y = api.rht_compose(sch, d, sg, xd)
+    torch.cuda.synchronize()
+    n = w["rows"]
+    idx = np.unique(np.concatenate([[0, n - 1], SAMPLE.choice(n, 96, replace=False)]))
+    y_ref = O.rht_compose(w["x"][idx].astype(np.float64), w["signs"].astype(float))
+    assert_rows_close(from_dev(y[torch.from_numpy(idx).cuda()]), y_ref, TOL["bf16"], "rht full")
+
+
+@pytest.mark.parametrize("sch", [(2, 2, 2, 2, 2, 2), (4, 16), (16, 2, 8)])
+def test_rht_fp32_schedules(sch):
+    d = int(np.prod(sch))
+    rng = np.random.default_rng(len(sch))
+    signs = np.where(rng.integers(0, 2, (2, d)) == 1, 1, -1).astype(np.int8)
+    x = rng.standard_normal((70, d)).astype(np.float32)
+    y = api.rht_compose(sch, d, signs_dev(signs), to_dev(x, "f32"))
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(y), O.rht_compose(x.astype(float), signs.astype(float)), 1e-5, f"rht {sch}")
+
+
+# ------------------------------------------------------------------ two-sided rotation
+def _two_sided_small():
+    rng = np.random.default_rng(31)
+    su, sv = (8, 3, 3), (8, 5, 2)
+    du, dv = 72, 80
+    out = {"su": su, "sv": sv, "du": du, "dv": dv}
+    out["tu"] = rng.standard_normal(sum(O.theta_counts(su, du))) * 0.05
+    out["tv"] = rng.standard_normal(sum(O.theta_counts(sv, dv))) * 0.05
+    out["gu"] = np.concatenate([rng.standard_normal(9)] * 2)
+    out["gv"] = rng.standard_normal(25)
+    out["su_s"] = np.where(rng.integers(0, 2, du) == 1, 1, -1).astype(np.int8)
+    out["sv_s"] = np.where(rng.integers(0, 2, dv) == 1, 1, -1).astype(np.int8)
+    out["w"] = W.round_io((rng.standard_normal((du, dv)) * 0.02).astype(np.float32), "bf16")
+    return out
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_small(use_ws, io):
+    c = _two_sided_small()
+    bu, su_ = gpu_blocks(api, c["su"], c["du"], c["tu"], c["gu"], "f32")
+    bv, sv_ = gpu_blocks(api, c["sv"], c["dv"], c["tv"], c["gv"], "f32")
+    ws = torch.empty(api.harp_rotate_weight_workspace(c["du"], c["dv"]) // 4, dtype=torch.float32,
+                     device="cuda") if use_ws else None
+    wd = to_dev(c["w"], io)
+    wt = api.harp_rotate_weight(c["su"], bu, None, signs_dev(c["su_s"]), c["sv"], bv, None, signs_dev(c["sv_s"]),
+                                wd, workspace=ws)
+    torch.cuda.synchronize()
+    obu = oracle_blocks(c["su"], c["du"], c["tu"], c["gu"], "f32")
+    obv = oracle_blocks(c["sv"], c["dv"], c["tv"], c["gv"], "f32")
+    ref = O.rotate_weight(c["w"].astype(float), c["su"], obu, c["su_s"].astype(float), c["sv"], obv,
+                          c["sv_s"].astype(float))
+    assert_rows_close(from_dev(wt), ref, TOL[io], "two-sided forward")
+    wtin = from_dev(wt)
+    back = api.harp_rotate_weight(c["su"], bu, None, signs_dev(c["su_s"]), c["sv"], bv, None,
+                                  signs_dev(c["sv_s"]), wt, inverse=True, workspace=ws)
+    torch.cuda.synchronize()
+    ref_b = O.rotate_weight(wtin, c["su"], obu, c["su_s"].astype(float), c["sv"], obv, c["sv_s"].astype(float),
+                            inverse=True)
+    assert_rows_close(from_dev(back), ref_b, TOL[io], "two-sided inverse")
+
+
+def test_rotate_weight_full_size_sampled():
+    w = _case("two_sided_13824x5120_bf16")
+    su, sv, du, dv = w["su"], w["schedule"], w["d_out"], w["d"]
+    bu, _ = gpu_blocks(api, su, du, w["theta_u"], w["gauss_u"], "f32")
+    bv, _ = gpu_blocks(api, sv, dv, w["theta_v"], w["gauss_v"], "f32")
+    wd = to_dev(w["x"], "bf16")
+    wt = api.harp_rotate_weight(su, bu, None, signs_dev(w["signs_u"]), sv, bv, None, signs_dev(w["signs_v"]), wd)
+    back = api.harp_rotate_weight(su, bu, None, signs_dev(w["signs_u"]), sv, bv, None, signs_dev(w["signs_v"]),
+                                  wt, inverse=True)
+    torch.cuda.synchronize()
+    # oracle on a sample of columns: V on every row, then U on the sampled columns
+    obu = oracle_blocks(su, du, w["theta_u"], w["gauss_u"], "f32")
+    obv = oracle_blocks(sv, dv, w["theta_v"], w["gauss_v"], "f32")
+    cols = np.sort(SAMPLE.choice(dv, 24, replace=False))
+    rowsv = O.apply(w["x"].astype(np.float64), sv, obv, w["signs_v"].astype(float))
+    ref_cols = O.apply(rowsv[:, cols].T, su, obu, w["signs_u"].astype(float))     # (24, du)
+    got_cols = from_dev(wt[:, torch.from_numpy(cols).cuda()]).T
+    assert_rows_close(got_cols, ref_cols, TOL["bf16"], "two-sided full (sampled columns)")
+    # round trip back to W
+    assert_rows_close(from_dev(back[:64]), w["x"][:64].astype(np.float64), 2 * TOL["bf16"], "two-sided roundtrip")
