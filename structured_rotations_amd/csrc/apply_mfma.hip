@@ -1,0 +1,529 @@
+// Matrix-core row kernel for the HARP transform (radices 2, 4, 5, 8; d <= 5120).
+//
+// HARP technical summary (gist.science 2605.29843), §2.1/§2.2: stage t
+// applies, to every group of coordinates that agree on all digits but digit
+// t, its own b_t x b_t orthogonal block.  Across a tile of 8 rows that is a
+// batch of tiny dense products, one per group, all with different blocks.
+// gfx950's v_mfma_f32_4x4x1f32 runs 16 independent 4x4 fp32 outer products
+// per instruction, so it carries these products with no padding and no
+// precision loss: a block of 4 lanes owns one group, lane i supplies row i's
+// input x[i][k] and the coefficient C[4h+i][k] (C = B, or B^T for the
+// inverse), and after b instructions (k = 0..b-1) the 4x4 result holds
+// output 4h+j of the group for the 4 rows of a row quad.  Each lane keeps
+// only 2b coefficients of its group (the block is spread over the 4 lanes),
+// loaded one round ahead, also across stage and tile boundaries.
+//
+// Layout.  The 8-row tile lives in LDS column-major: a column is 8 fp32
+// (32 bytes); columns are XOR-swizzled in groups of 8 and the two row quads
+// of a column swap places every other group of 8 columns, so 16-byte accesses
+// spread over all 64 banks for every digit stride.
+//
+// Roles.  Waves 0..7 compute.  Waves 8..11 move data: while the compute
+// waves run the stages of tile n they stream tile n+1 from HBM into
+// registers (their outstanding loads never stall the compute waves, whose
+// wait counters only see coefficient loads), and between tiles they write it
+// into LDS.  When the last stage is contiguous (digit stride 1, radix 8) the
+// compute waves store its result straight to HBM: the MFMA operands are
+// swapped for that stage so each lane ends with 8 consecutive outputs of one
+// row.  Otherwise the data waves copy the finished tile out.  The sign flip
+// is folded into the tile input (forward) or output (inverse).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace harp {
+
+namespace {
+
+constexpr int kRows = 8;             // rows per tile (two row quads)
+
+// Wave roles: CW compute waves, IOW data waves, each data thread prefetching
+// up to MIO 4-row x 16-byte micro-blocks of the next tile into registers.
+template <int CW, int IOW, int MIO>
+struct Roles {
+  static constexpr int kCompWaves = CW;
+  static constexpr int kThreads = 64 * (CW + IOW);
+  static constexpr int kIoThreads = 64 * IOW;
+  static constexpr int kMaxIo = MIO;
+  static constexpr int kGroupsPerRound = 16 * CW;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct StageFast {
+  int b;
+  int s;
+  int blk_off;
+  int grp_off;
+  uint64_t div_s;   // floor(2^32 / s) + 1: n / s == (n * div_s) >> 32 for n, s < 2^16
+};
+
+struct MfmaParams {
+  int d;
+  int m;
+  int transpose;
+  int sign_mode;     // 0 none, 1 on input, 2 on output
+  int n_io;          // micro-blocks per tile
+  int chunks;        // 16-byte chunks per row
+  int direct_out;    // last stage stores straight to HBM
+  int roles;         // 0: 8 compute + 4 data waves; 1: 4 + 4
+  StageFast st[kMaxStagesDev];
+  const void* blocks;
+  const float* scales;
+  const int8_t* signs;
+  const void* x;
+  int64_t ldx;
+  void* y;
+  int64_t ldy;
+  int64_t rows;
+  int64_t ntiles;
+};
+
+__device__ __forceinline__ int fdiv(int n, uint64_t magic) { return (int)(((uint64_t)(uint32_t)n * magic) >> 32); }
+
+// LDS address (in floats) of element (col, row) of the tile.
+__device__ __forceinline__ int eaddr(int col, int row) {
+  const int pc = col ^ ((col >> 3) & 7);
+  return pc * 8 + (row ^ (((col >> 3) & 1) << 2));
+}
+// address of the 4-row quad q of column col (16-byte aligned)
+__device__ __forceinline__ int qaddr(int col, int q) { return eaddr(col, 4 * q); }
+
+template <typename T> struct Io;
+template <> struct Io<uint16_t> { static constexpr int V = 8; };
+template <> struct Io<float> { static constexpr int V = 4; };
+
+__device__ __forceinline__ float sgnf(float v, int8_t s) {
+  return __uint_as_float(__float_as_uint(v) ^ (s < 0 ? 0x80000000u : 0u));
+}
+
+template <typename T>
+__device__ __forceinline__ float elem(const u32x4& w, int u);
+template <>
+__device__ __forceinline__ float elem<uint16_t>(const u32x4& w, int u) {
+  const uint32_t word = u < 2 ? w.x : (u < 4 ? w.y : (u < 6 ? w.z : w.w));
+  return (u & 1) ? bf16_hi(word) : bf16_lo(word);
+}
+template <>
+__device__ __forceinline__ float elem<float>(const u32x4& w, int u) {
+  return __uint_as_float(u == 0 ? w.x : (u == 1 ? w.y : (u == 2 ? w.z : w.w)));
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack_row(const float* v);
+template <>
+__device__ __forceinline__ u32x4 pack_row<uint16_t>(const float* v) {
+  return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+template <>
+__device__ __forceinline__ u32x4 pack_row<float>(const float* v) {
+  return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+}
+
+// ---------------------------------------------------------------- data waves
+// Micro-block mb = (row quad q, 16-byte chunk c): rows 4q..4q+3 x V columns.
+template <typename T>
+__device__ __forceinline__ void io_load(const MfmaParams& p, int64_t row0, int nr, int mb, u32x4 (&w)[4]) {
+  constexpr int V = Io<T>::V;
+  const T* x = static_cast<const T*>(p.x);
+  const int q = mb / p.chunks;
+  const int c = mb - q * p.chunks;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * q + i;
+    if (r < nr) w[i] = ld_stream(x + (row0 + r) * p.ldx + (int64_t)c * V);
+    else w[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void io_to_lds(const MfmaParams& p, float* tile, int mb, const u32x4 (&w)[4]) {
+  constexpr int V = Io<T>::V;
+  const int q = mb / p.chunks;
+  const int c = mb - q * p.chunks;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int col = c * V + u;
+    f32x4 v;
+    v.x = elem<T>(w[0], u); v.y = elem<T>(w[1], u); v.z = elem<T>(w[2], u); v.w = elem<T>(w[3], u);
+    if (p.sign_mode == 1) {
+      const int8_t s = p.signs[col];
+      v.x = sgnf(v.x, s); v.y = sgnf(v.y, s); v.z = sgnf(v.z, s); v.w = sgnf(v.w, s);
+    }
+    *reinterpret_cast<f32x4*>(tile + qaddr(col, q)) = v;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void io_store(const MfmaParams& p, const float* tile, int64_t row0, int nr, int mb) {
+  constexpr int V = Io<T>::V;
+  T* y = static_cast<T*>(p.y);
+  const int q = mb / p.chunks;
+  const int c = mb - q * p.chunks;
+  float v[4][V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int col = c * V + u;
+    f32x4 t = *reinterpret_cast<const f32x4*>(tile + qaddr(col, q));
+    if (p.sign_mode == 2) {
+      const int8_t s = p.signs[col];
+      t.x = sgnf(t.x, s); t.y = sgnf(t.y, s); t.z = sgnf(t.z, s); t.w = sgnf(t.w, s);
+    }
+    v[0][u] = t.x; v[1][u] = t.y; v[2][u] = t.z; v[3][u] = t.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * q + i;
+    if (r < nr) st_stream(y + (row0 + r) * p.ldy + (int64_t)c * V, pack_row<T>(v[i]));
+  }
+}
+
+// ---------------------------------------------------------------- coefficients
+// cf[h][k] = C[4h + j][k] of group g (C = B forward, B^T inverse); zero
+// outside the radix or for an idle lane.
+template <int B, typename TB, bool TR>
+__device__ __forceinline__ void load_coef(const MfmaParams& p, const StageFast& sd, int g, int j, bool valid,
+                                          float (&cf)[2][8]) {
+  const TB* blk = static_cast<const TB*>(p.blocks) + sd.blk_off + (int64_t)g * B * B;
+  float scale = 1.0f;
+  if constexpr (std::is_same<TB, int8_t>::value) scale = valid ? p.scales[sd.grp_off + g] : 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cf[h][k] = 0.0f;
+  if (!valid) return;
+  constexpr bool kVec = (B == 8 || B == 4);
+  if constexpr (kVec && !TR) {
+#pragma unroll
+    for (int h = 0; h < (B == 8 ? 2 : 1); ++h) {
+      const TB* row = blk + (4 * h + j) * B;
+      if constexpr (std::is_same<TB, float>::value) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(row);
+        cf[h][0] = __uint_as_float(a.x); cf[h][1] = __uint_as_float(a.y);
+        cf[h][2] = __uint_as_float(a.z); cf[h][3] = __uint_as_float(a.w);
+        if constexpr (B == 8) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(row + 4);
+          cf[h][4] = __uint_as_float(b.x); cf[h][5] = __uint_as_float(b.y);
+          cf[h][6] = __uint_as_float(b.z); cf[h][7] = __uint_as_float(b.w);
+        }
+      } else if constexpr (std::is_same<TB, uint16_t>::value) {
+        if constexpr (B == 8) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(row);
+          cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
+          cf[h][4] = bf16_lo(a.z); cf[h][5] = bf16_hi(a.z); cf[h][6] = bf16_lo(a.w); cf[h][7] = bf16_hi(a.w);
+        } else {
+          const uint2 a = *reinterpret_cast<const uint2*>(row);
+          cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
+        }
+      } else {
+        uint32_t wd[2];
+        if constexpr (B == 8) {
+          const uint2 a = *reinterpret_cast<const uint2*>(row);
+          wd[0] = a.x; wd[1] = a.y;
+        } else {
+          wd[0] = *reinterpret_cast<const uint32_t*>(row);
+          wd[1] = 0;
+        }
+#pragma unroll
+        for (int k = 0; k < B; ++k) cf[h][k] = (float)(int8_t)(wd[k >> 2] >> (8 * (k & 3))) * scale;
+      }
+    }
+  } else {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int o = 4 * h + j;
+#pragma unroll
+    for (int k = 0; k < B; ++k)
+      if (o < B) cf[h][k] = coef<TB>(blk, TR ? k * B + o : o * B + k, scale);
+  }
+  }
+}
+
+template <typename TB, bool TR>
+__device__ __forceinline__ void load_coef_any(const MfmaParams& p, const StageFast& sd, int g, int j, bool valid,
+                                              float (&cf)[2][8]) {
+  switch (sd.b) {
+    case 2: load_coef<2, TB, TR>(p, sd, g, j, valid, cf); break;
+    case 4: load_coef<4, TB, TR>(p, sd, g, j, valid, cf); break;
+    case 5: load_coef<5, TB, TR>(p, sd, g, j, valid, cf); break;
+    default: load_coef<8, TB, TR>(p, sd, g, j, valid, cf); break;
+  }
+}
+
+// ---------------------------------------------------------------- compute waves
+// One stage over the tile.  cf holds round 0's coefficients on entry and the
+// next stage's (or, after the last stage, the next tile's first) on exit.
+template <int B, typename T, typename TB, bool TR, bool DIRECT, int kGroupsPerRound>
+__device__ void mfma_stage(const MfmaParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
+  constexpr int NH = B > 4 ? 2 : 1;
+  const StageFast& sd = p.st[t];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int bk = lane >> 2;
+  const int j = lane & 3;
+  const int ngroups = p.d / B;
+  const int s = sd.s;
+  float nx[2][8];
+  for (int base_g = 0; base_g < ngroups; base_g += kGroupsPerRound) {
+    const int g = base_g + wave * 16 + bk;
+    const bool valid = g < ngroups;
+    // prefetch the next round (or the next stage's / next tile's first round)
+    {
+      const int nb = base_g + kGroupsPerRound;
+      if (nb < ngroups) {
+        const int gn = nb + wave * 16 + bk;
+        load_coef<B, TB, TR>(p, sd, gn < ngroups ? gn : 0, j, gn < ngroups, nx);
+      } else {
+        const int tn = t + 1 < p.m ? t + 1 : 0;
+        const StageFast& sn = p.st[tn];
+        const int gn = wave * 16 + bk;
+        const int ngn = p.d / sn.b;
+        load_coef_any<TB, TR>(p, sn, gn < ngn ? gn : 0, j, gn < ngn, nx);
+      }
+    }
+    const int gg = valid ? g : 0;
+    const int hi = fdiv(gg, sd.div_s);
+    const int col0 = hi * (B - 1) * s + gg;     // = hi * B * s + (gg - hi * s)
+#pragma unroll
+    for (int q = 0; q < kRows / 4; ++q) {
+      float xv[B];
+#pragma unroll
+      for (int k = 0; k < B; ++k) xv[k] = tile[eaddr(col0 + k * s, 4 * q + j)];
+      f32x4 acc[2];
+      if constexpr (!DIRECT) {
+        // D[i][j] = sum_k x[row i][k] C[4h+j][k]: lane j holds output 4h+j for the quad's rows
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < B; ++k) acc[h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[k], cf[h][k], acc[h], 0, 0, 0);
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const int o = 4 * h + j;
+          if (valid && o < B) *reinterpret_cast<f32x4*>(tile + qaddr(col0 + o * s, q)) = acc[h];
+        }
+      } else {
+        // D[i][j] = sum_k C[4h+i][k] x[row j][k]: lane j holds outputs 4h..4h+3 of row 4q+j
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < B; ++k) acc[h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][k], xv[k], acc[h], 0, 0, 0);
+        }
+        const int r = 4 * q + j;
+        if (valid && r < nr) {
+          float v[8] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w, acc[1].x, acc[1].y, acc[1].z, acc[1].w};
+          T* y = static_cast<T*>(p.y) + (row0 + r) * p.ldy + col0;
+          if constexpr (std::is_same<T, uint16_t>::value) {
+            st_stream(y, pack_row<T>(v));
+          } else {
+            st_stream(y, pack_row<T>(v));
+            st_stream(y + 4, pack_row<T>(v + 4));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cf[h][k] = nx[h][k];
+  }
+}
+
+template <typename T, typename TB, bool TR, int GPR>
+__device__ void run_stage(const MfmaParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
+  if (p.direct_out && t == p.m - 1) {
+    mfma_stage<8, T, TB, TR, true, GPR>(p, t, tile, cf, row0, nr);
+    return;
+  }
+  switch (p.st[t].b) {
+    case 2: mfma_stage<2, T, TB, TR, false, GPR>(p, t, tile, cf, row0, nr); break;
+    case 4: mfma_stage<4, T, TB, TR, false, GPR>(p, t, tile, cf, row0, nr); break;
+    case 5: mfma_stage<5, T, TB, TR, false, GPR>(p, t, tile, cf, row0, nr); break;
+    case 8: mfma_stage<8, T, TB, TR, false, GPR>(p, t, tile, cf, row0, nr); break;
+    default: break;
+  }
+}
+
+__device__ __forceinline__ int tile_rows(const MfmaParams& p, int64_t tix) {
+  const int64_t left = p.rows - tix * kRows;
+  return left < kRows ? (int)left : kRows;
+}
+
+template <typename T, typename TB, bool TR, typename RL>
+__global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) {
+  constexpr int kCompWaves = RL::kCompWaves;
+  constexpr int kIoThreads = RL::kIoThreads;
+  constexpr int kMaxIo = RL::kMaxIo;
+  extern __shared__ float tile[];
+  const bool io_wave = threadIdx.x >= 64 * kCompWaves;
+  int64_t tix = blockIdx.x;
+  if (tix >= p.ntiles) return;   // uniform per workgroup
+  if (io_wave) {
+    const int it = threadIdx.x - 64 * kCompWaves;
+    u32x4 w[kMaxIo][4];
+    // first tile: load and write
+    {
+      const int nr = tile_rows(p, tix);
+      for (int mb = it; mb < p.n_io; mb += kIoThreads) {
+        u32x4 one[4];
+        io_load<T>(p, tix * kRows, nr, mb, one);
+        io_to_lds<T>(p, tile, mb, one);
+      }
+    }
+    __syncthreads();
+    for (; tix < p.ntiles; tix += gridDim.x) {
+      const int64_t row0 = tix * kRows;
+      const int nr = tile_rows(p, tix);
+      const int64_t nxt = tix + gridDim.x;
+      const bool has_next = nxt < p.ntiles;
+      const int nr_next = has_next ? tile_rows(p, nxt) : 0;
+      // stream the next tile into registers while the stages run
+      if (has_next) {
+#pragma unroll
+        for (int u = 0; u < kMaxIo; ++u) {
+          const int mb = it + u * kIoThreads;
+          if (mb < p.n_io) io_load<T>(p, nxt * kRows, nr_next, mb, w[u]);
+        }
+      }
+      for (int t = 0; t < p.m; ++t) __syncthreads();
+      if (!p.direct_out) {
+        for (int mb = it; mb < p.n_io; mb += kIoThreads) io_store<T>(p, tile, row0, nr, mb);
+        __syncthreads();
+      }
+      if (has_next) {
+#pragma unroll
+        for (int u = 0; u < kMaxIo; ++u) {
+          const int mb = it + u * kIoThreads;
+          if (mb < p.n_io) io_to_lds<T>(p, tile, mb, w[u]);
+        }
+        for (int mb = it + kMaxIo * kIoThreads; mb < p.n_io; mb += kIoThreads) {
+          u32x4 one[4];
+          io_load<T>(p, nxt * kRows, nr_next, mb, one);
+          io_to_lds<T>(p, tile, mb, one);
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float cf[2][8];
+    {
+      const int g0 = wave * 16 + (lane >> 2);
+      const int ng0 = p.d / p.st[0].b;
+      load_coef_any<TB, TR>(p, p.st[0], g0 < ng0 ? g0 : 0, lane & 3, g0 < ng0, cf);
+    }
+    __syncthreads();
+    for (; tix < p.ntiles; tix += gridDim.x) {
+      const int64_t row0 = tix * kRows;
+      const int nr = tile_rows(p, tix);
+      for (int t = 0; t < p.m; ++t) {
+        run_stage<T, TB, TR, RL::kGroupsPerRound>(p, t, tile, cf, row0, nr);
+        __syncthreads();
+      }
+      if (!p.direct_out) __syncthreads();
+      __syncthreads();
+    }
+  }
+}
+
+int cu_count_mfma() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      return 256;
+  }
+  return cus;
+}
+
+template <typename T, typename TB, typename RL>
+hipError_t launch_mfma_roles(const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
+  auto kern = p.transpose ? apply_mfma_kernel<T, TB, true, RL> : apply_mfma_kernel<T, TB, false, RL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(RL::kThreads), lds, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, typename TB>
+hipError_t launch_mfma_typed(const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
+  if (p.roles == 1) return launch_mfma_roles<T, TB, Roles<4, 4, 5>>(p, grid, lds, st);
+  return launch_mfma_roles<T, TB, Roles<8, 4, 2>>(p, grid, lds, st);
+}
+
+template <typename T>
+hipError_t launch_mfma_blk(DT bdt, const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
+  switch (bdt) {
+    case DT::F32: return launch_mfma_typed<T, float>(p, grid, lds, st);
+    case DT::BF16: return launch_mfma_typed<T, uint16_t>(p, grid, lds, st);
+    case DT::I8: return launch_mfma_typed<T, int8_t>(p, grid, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool mfma_path_supported(const Plan& pl, DT io, const void* blocks, const void* x, int64_t ldx, const void* y,
+                         int64_t ldy) {
+  if (io != DT::F32 && io != DT::BF16) return false;
+  if (reinterpret_cast<uintptr_t>(blocks) % 16 != 0) return false;
+  if (pl.d % 64 != 0 || pl.d > 5120) return false;
+  for (int t = 0; t < pl.m; ++t) {
+    const int b = pl.radix[t];
+    if (b != 2 && b != 4 && b != 5 && b != 8) return false;
+  }
+  const int eb = io_bytes(io);
+  if ((ldx * eb) % 16 || (ldy * eb) % 16) return false;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16) return false;
+  return true;
+}
+
+hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
+                             const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
+                             int64_t rows, int roles, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  MfmaParams p{};
+  p.d = (int)pl.d;
+  p.m = pl.m;
+  p.transpose = inverse ? 1 : 0;
+  p.sign_mode = signs ? (inverse ? 2 : 1) : 0;
+  for (int i = 0; i < pl.m; ++i) {
+    const int t = inverse ? pl.m - 1 - i : i;
+    StageFast& sf = p.st[i];
+    sf.b = pl.radix[t];
+    sf.s = (int)pl.stride[t];
+    sf.blk_off = (int)pl.blk_off[t];
+    sf.grp_off = (int)pl.grp_off[t];
+    sf.div_s = (uint64_t)((1ull << 32) / (uint64_t)sf.s) + 1ull;
+  }
+  const StageFast& last = p.st[pl.m - 1];
+  p.direct_out = (last.s == 1 && last.b == 8 && p.sign_mode != 2) ? 1 : 0;
+  const int V = io == DT::BF16 ? 8 : 4;
+  p.chunks = (int)(pl.d / V);
+  p.blocks = blocks;
+  p.scales = scales;
+  p.signs = signs;
+  p.x = x;
+  p.ldx = ldx;
+  p.y = y;
+  p.ldy = ldy;
+  p.rows = rows;
+  p.roles = roles;
+  p.n_io = (kRows / 4) * p.chunks;
+  p.ntiles = (rows + kRows - 1) / kRows;
+  const size_t lds = (size_t)kRows * pl.d * sizeof(float);
+  int64_t grid = cu_count_mfma();
+  if (grid > p.ntiles) grid = p.ntiles;
+  if (io == DT::BF16) return launch_mfma_blk<uint16_t>(bdt, p, (int)grid, lds, stream);
+  return launch_mfma_blk<float>(bdt, p, (int)grid, lds, stream);
+}
+
+}  // namespace harp

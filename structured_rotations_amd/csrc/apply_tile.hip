@@ -12,6 +12,7 @@
 // Any schedule (radices 2..16, d <= 32768), fp32 or bf16 rows, fp32 / bf16 /
 // int8+scale blocks.  The inverse runs the stages in reverse order with
 // transposed blocks and applies the sign on the output side.
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -139,6 +140,16 @@ __global__ void __launch_bounds__(512) apply_tile_kernel(TileParams p) {
 
 namespace {
 
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && v[0] != '\0' && v[0] != '0';
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return (v != nullptr && v[0] != '\0') ? std::atoi(v) : dflt;
+}
+
 int device_cu_count() {
   static int cus = 0;
   if (cus == 0) {
@@ -178,6 +189,10 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
                              int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
                              int64_t rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if (in_dt == out_dt && !env_flag("HARP_FORCE_GENERIC") && mfma_path_supported(pl, in_dt, blocks, x, ldx, y, ldy)) {
+    static const int roles = env_int("HARP_MFMA_ROLES", 0);
+    return launch_apply_mfma(pl, inverse, blocks, bdt, scales, signs, x, ldx, in_dt, y, ldy, rows, roles, stream);
+  }
   TileParams p{};
   p.d = (int)pl.d;
   p.ldsrow = (int)((pl.d + 63) / 64 * 64);

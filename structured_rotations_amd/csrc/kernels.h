@@ -22,6 +22,15 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
                              int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
                              int64_t rows, hipStream_t stream);
 
+// Matrix-core row kernel (radices <= 8, d % 64 == 0, d <= 5120, 16-byte
+// aligned rows and blocks, same I/O dtype on both sides).  roles selects the
+// wave split (0: 8 compute + 4 data waves, 1: 4 + 4).
+bool mfma_path_supported(const Plan& pl, DT io, const void* blocks, const void* x, int64_t ldx, const void* y,
+                         int64_t ldy);
+hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
+                             const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
+                             int64_t rows, int roles, hipStream_t stream);
+
 // Column passes of the two-sided rotation: apply stages [t0, t1) of the
 // schedule `pl` (acting on the row index of a pl.d x ncols matrix) to every
 // column.  Forward order (inverse=false) or transposed blocks in reverse
