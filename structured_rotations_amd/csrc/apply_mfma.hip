@@ -8,25 +8,25 @@
 // per instruction, so it carries these products with no padding and no
 // precision loss: a block of 4 lanes owns one group, lane i supplies row i's
 // input x[i][k] and the coefficient C[4h+i][k] (C = B, or B^T for the
-// inverse), and after b instructions (k = 0..b-1) the 4x4 result holds
-// output 4h+j of the group for the 4 rows of a row quad.  Each lane keeps
-// only 2b coefficients of its group (the block is spread over the 4 lanes),
-// loaded one round ahead, also across stage and tile boundaries.
+// inverse); after b instructions (k = 0..b-1) lane j holds output 4h+j of the
+// group for the 4 rows of a row quad.  Each lane keeps 2b coefficients of its
+// group in registers, loaded one round ahead, also across stage and tile
+// boundaries.
 //
-// Layout.  The 8-row tile lives in LDS column-major: a column is 8 fp32
-// (32 bytes); columns are XOR-swizzled in groups of 8 and the two row quads
-// of a column swap places every other group of 8 columns, so 16-byte accesses
-// spread over all 64 banks for every digit stride.
+// Layout.  No permutation is ever materialised: the 8-row tile sits in LDS
+// as two row-quad planes of 16-byte units (one column's 4 rows), columns
+// XOR-swizzled so that the 4-byte input gathers of every digit stride spread
+// over all banks; each stage reads its groups' columns at digit stride s_t and
+// writes the results back in place.
 //
-// Roles.  Waves 0..7 compute.  Waves 8..11 move data: while the compute
-// waves run the stages of tile n they stream tile n+1 from HBM into
-// registers (their outstanding loads never stall the compute waves, whose
-// wait counters only see coefficient loads), and between tiles they write it
-// into LDS.  When the last stage is contiguous (digit stride 1, radix 8) the
-// compute waves store its result straight to HBM: the MFMA operands are
-// swapped for that stage so each lane ends with 8 consecutive outputs of one
-// row.  Otherwise the data waves copy the finished tile out.  The sign flip
-// is folded into the tile input (forward) or output (inverse).
+// Roles.  Waves 0..7 compute.  Waves 8..15 move data: while the compute waves
+// run the stages of tile n they stream tile n+1 (and its sign bytes) from
+// HBM into registers -- their outstanding loads never stall the compute
+// waves, whose wait counters only see coefficient loads -- and between tiles
+// they write it into LDS.  When the last stage is contiguous (digit stride 1,
+// radix 8) the compute waves store its result straight to HBM, with the MFMA
+// operands swapped for that stage so each lane ends with 8 consecutive
+// outputs of one row; otherwise the data waves copy the finished tile out.
 #include <type_traits>
 
 #include "common.h"
@@ -36,10 +36,10 @@ namespace harp {
 
 namespace {
 
-constexpr int kRows = 8;             // rows per tile (two row quads)
+constexpr int kRows = 8;   // rows per tile (two row quads)
 
 // Wave roles: CW compute waves, IOW data waves, each data thread prefetching
-// up to MIO 4-row x 16-byte micro-blocks of the next tile into registers.
+// up to MIO 16-byte chunks per row quad of the next tile into registers.
 template <int CW, int IOW, int MIO>
 struct Roles {
   static constexpr int kCompWaves = CW;
@@ -54,9 +54,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct StageFast {
   int b;
   int s;
+  int G;            // groups = d / b
   int blk_off;
   int grp_off;
   uint64_t div_s;   // floor(2^32 / s) + 1: n / s == (n * div_s) >> 32 for n, s < 2^16
+  uint64_t div_b;
 };
 
 struct MfmaParams {
@@ -64,10 +66,9 @@ struct MfmaParams {
   int m;
   int transpose;
   int sign_mode;     // 0 none, 1 on input, 2 on output
-  int n_io;          // micro-blocks per tile
   int chunks;        // 16-byte chunks per row
   int direct_out;    // last stage stores straight to HBM
-  int roles;         // 0: 8 compute + 4 data waves; 1: 4 + 4
+  int roles;         // 0: 8 compute + 8 data waves; 1: 8 + 4
   StageFast st[kMaxStagesDev];
   const void* blocks;
   const float* scales;
@@ -81,22 +82,19 @@ struct MfmaParams {
 };
 
 __device__ __forceinline__ int fdiv(int n, uint64_t magic) { return (int)(((uint64_t)(uint32_t)n * magic) >> 32); }
-
-// LDS address (in floats) of element (col, row) of the tile.
-__device__ __forceinline__ int eaddr(int col, int row) {
-  const int pc = col ^ ((col >> 3) & 7);
-  return pc * 8 + (row ^ (((col >> 3) & 1) << 2));
-}
-// address of the 4-row quad q of column col (16-byte aligned)
-__device__ __forceinline__ int qaddr(int col, int q) { return eaddr(col, 4 * q); }
+// LDS layout (one order for every stage, so each stage updates the tile in
+// place): two row-quad planes, plane q (rows 4q..4q+3) at q * 4d floats; in
+// a plane, column c's 4 rows form one 16-byte unit at unit index pcol(c).
+// pcol XORs bits 0..3 of c with bits 3..6 (bijective inside every 16
+// columns); for digit strides 512, 64, 8 and 1 the 4-byte gathers of a wave
+// hit every bank once.
+__device__ __forceinline__ int pcol(int c) { return c ^ ((c >> 3) & 15); }
 
 template <typename T> struct Io;
 template <> struct Io<uint16_t> { static constexpr int V = 8; };
 template <> struct Io<float> { static constexpr int V = 4; };
 
-__device__ __forceinline__ float sgnf(float v, int8_t s) {
-  return __uint_as_float(__float_as_uint(v) ^ (s < 0 ? 0x80000000u : 0u));
-}
+__device__ __forceinline__ float sgnf(float v, uint32_t negbit) { return __uint_as_float(__float_as_uint(v) ^ negbit); }
 
 template <typename T>
 __device__ __forceinline__ float elem(const u32x4& w, int u);
@@ -122,53 +120,67 @@ __device__ __forceinline__ u32x4 pack_row<float>(const float* v) {
 }
 
 // ---------------------------------------------------------------- data waves
-// Micro-block mb = (row quad q, 16-byte chunk c): rows 4q..4q+3 x V columns.
+// Micro-block mb = (row quad q, 16-byte chunk c): rows 4q..4q+3 x V columns,
+// plus the V sign bytes of those columns (zero = no flip).
+struct IoBlock {
+  u32x4 w[4];
+  uint2 sg;
+};
+
 template <typename T>
-__device__ __forceinline__ void io_load(const MfmaParams& p, int64_t row0, int nr, int mb, u32x4 (&w)[4]) {
+__device__ __forceinline__ void io_load(const MfmaParams& p, int64_t row0, int nr, int q, int c, IoBlock& blk) {
   constexpr int V = Io<T>::V;
   const T* x = static_cast<const T*>(p.x);
-  const int q = mb / p.chunks;
-  const int c = mb - q * p.chunks;
+  // rows past the end of a ragged last tile re-read the last row: they are
+  // transformed like the others but never stored
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 4 * q + i;
-    if (r < nr) w[i] = ld_stream(x + (row0 + r) * p.ldx + (int64_t)c * V);
-    else w[i] = u32x4{0u, 0u, 0u, 0u};
+    const int r = 4 * q + i < nr ? 4 * q + i : nr - 1;
+    blk.w[i] = ld_stream(x + (row0 + r) * p.ldx + (int64_t)c * V);
+  }
+  blk.sg = uint2{0u, 0u};
+  if (p.sign_mode == 1) {
+    const int8_t* sp = p.signs + c * V;
+    if constexpr (V == 8) blk.sg = *reinterpret_cast<const uint2*>(sp);
+    else blk.sg.x = *reinterpret_cast<const uint32_t*>(sp);
   }
 }
 
 template <typename T>
-__device__ __forceinline__ void io_to_lds(const MfmaParams& p, float* tile, int mb, const u32x4 (&w)[4]) {
+__device__ __forceinline__ f32x4 io_column(const IoBlock& blk, int u) {
+  // sign byte u (0x01 or 0xff): bit 7 set for -1
+  const uint32_t neg = (((u < 4 ? blk.sg.x : blk.sg.y) >> (8 * (u & 3))) & 0x80u) << 24;
+  f32x4 v;
+  v.x = sgnf(elem<T>(blk.w[0], u), neg); v.y = sgnf(elem<T>(blk.w[1], u), neg);
+  v.z = sgnf(elem<T>(blk.w[2], u), neg); v.w = sgnf(elem<T>(blk.w[3], u), neg);
+  return v;
+}
+
+// Writes a micro-block (rows 4q..4q+3 of the V columns of chunk c).  The
+// chunk's columns c*V + u share bits 3..6 (V <= 8 and chunks are aligned), so
+// their units are (c*V ^ m) ^ u with one mask m.
+template <typename T>
+__device__ __forceinline__ void io_to_lds(const MfmaParams& p, float* tile, int q, int c, const IoBlock& blk) {
   constexpr int V = Io<T>::V;
-  const int q = mb / p.chunks;
-  const int c = mb - q * p.chunks;
+  float* plane = tile + q * 4 * p.d;
+  const int base = pcol(c * V);
 #pragma unroll
-  for (int u = 0; u < V; ++u) {
-    const int col = c * V + u;
-    f32x4 v;
-    v.x = elem<T>(w[0], u); v.y = elem<T>(w[1], u); v.z = elem<T>(w[2], u); v.w = elem<T>(w[3], u);
-    if (p.sign_mode == 1) {
-      const int8_t s = p.signs[col];
-      v.x = sgnf(v.x, s); v.y = sgnf(v.y, s); v.z = sgnf(v.z, s); v.w = sgnf(v.w, s);
-    }
-    *reinterpret_cast<f32x4*>(tile + qaddr(col, q)) = v;
-  }
+  for (int u = 0; u < V; ++u)
+    *reinterpret_cast<f32x4*>(plane + 4 * (base ^ u)) = io_column<T>(blk, u);
 }
 
 template <typename T>
-__device__ __forceinline__ void io_store(const MfmaParams& p, const float* tile, int64_t row0, int nr, int mb) {
+__device__ __forceinline__ void io_store(const MfmaParams& p, const float* tile, int64_t row0, int nr, int q, int c) {
   constexpr int V = Io<T>::V;
   T* y = static_cast<T*>(p.y);
-  const int q = mb / p.chunks;
-  const int c = mb - q * p.chunks;
+  const float* plane = tile + q * 4 * p.d;
   float v[4][V];
 #pragma unroll
   for (int u = 0; u < V; ++u) {
     const int col = c * V + u;
-    f32x4 t = *reinterpret_cast<const f32x4*>(tile + qaddr(col, q));
-    if (p.sign_mode == 2) {
-      const int8_t s = p.signs[col];
-      t.x = sgnf(t.x, s); t.y = sgnf(t.y, s); t.z = sgnf(t.z, s); t.w = sgnf(t.w, s);
+    f32x4 t = *reinterpret_cast<const f32x4*>(plane + 4 * pcol(col));
+    if (p.sign_mode == 2 && p.signs[col] < 0) {
+      t.x = -t.x; t.y = -t.y; t.z = -t.z; t.w = -t.w;
     }
     v[0][u] = t.x; v[1][u] = t.y; v[2][u] = t.z; v[3][u] = t.w;
   }
@@ -231,12 +243,12 @@ __device__ __forceinline__ void load_coef(const MfmaParams& p, const StageFast& 
     }
   } else {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int o = 4 * h + j;
+    for (int h = 0; h < 2; ++h) {
+      const int o = 4 * h + j;
 #pragma unroll
-    for (int k = 0; k < B; ++k)
-      if (o < B) cf[h][k] = coef<TB>(blk, TR ? k * B + o : o * B + k, scale);
-  }
+      for (int k = 0; k < B; ++k)
+        if (o < B) cf[h][k] = coef<TB>(blk, TR ? k * B + o : o * B + k, scale);
+    }
   }
 }
 
@@ -254,7 +266,7 @@ __device__ __forceinline__ void load_coef_any(const MfmaParams& p, const StageFa
 // ---------------------------------------------------------------- compute waves
 // One stage over the tile.  cf holds round 0's coefficients on entry and the
 // next stage's (or, after the last stage, the next tile's first) on exit.
-template <int B, typename T, typename TB, bool TR, bool DIRECT, int kGroupsPerRound>
+template <int B, typename T, typename TB, bool TR, bool DIRECT, int GPR>
 __device__ void mfma_stage(const MfmaParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
   constexpr int NH = B > 4 ? 2 : 1;
   const StageFast& sd = p.st[t];
@@ -262,59 +274,75 @@ __device__ void mfma_stage(const MfmaParams& p, int t, float* tile, float (&cf)[
   const int wave = threadIdx.x >> 6;
   const int bk = lane >> 2;
   const int j = lane & 3;
-  const int ngroups = p.d / B;
+  const int ngroups = sd.G;
   const int s = sd.s;
+  const int plane = 4 * p.d;                  // floats between the two row quads
   float nx[2][8];
-  for (int base_g = 0; base_g < ngroups; base_g += kGroupsPerRound) {
+  for (int base_g = 0; base_g < ngroups; base_g += GPR) {
     const int g = base_g + wave * 16 + bk;
     const bool valid = g < ngroups;
     // prefetch the next round (or the next stage's / next tile's first round)
     {
-      const int nb = base_g + kGroupsPerRound;
+      const int nb = base_g + GPR;
       if (nb < ngroups) {
         const int gn = nb + wave * 16 + bk;
         load_coef<B, TB, TR>(p, sd, gn < ngroups ? gn : 0, j, gn < ngroups, nx);
       } else {
-        const int tn = t + 1 < p.m ? t + 1 : 0;
-        const StageFast& sn = p.st[tn];
+        const StageFast& sn = p.st[t + 1 < p.m ? t + 1 : 0];
         const int gn = wave * 16 + bk;
-        const int ngn = p.d / sn.b;
-        load_coef_any<TB, TR>(p, sn, gn < ngn ? gn : 0, j, gn < ngn, nx);
+        load_coef_any<TB, TR>(p, sn, gn < sn.G ? gn : 0, j, gn < sn.G, nx);
       }
     }
     const int gg = valid ? g : 0;
     const int hi = fdiv(gg, sd.div_s);
     const int col0 = hi * (B - 1) * s + gg;     // = hi * B * s + (gg - hi * s)
+    const float* src = tile + j;
+    float xv[2][B];
 #pragma unroll
-    for (int q = 0; q < kRows / 4; ++q) {
-      float xv[B];
+    for (int k = 0; k < B; ++k) {
+      const int a = 4 * pcol(col0 + k * s);
+      xv[0][k] = src[a];
+      xv[1][k] = src[a + plane];
+    }
+    f32x4 acc[2][2];
 #pragma unroll
-      for (int k = 0; k < B; ++k) xv[k] = tile[eaddr(col0 + k * s, 4 * q + j)];
-      f32x4 acc[2];
-      if constexpr (!DIRECT) {
-        // D[i][j] = sum_k x[row i][k] C[4h+j][k]: lane j holds output 4h+j for the quad's rows
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < NH; ++h) acc[q][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!DIRECT) {
+      // D[i][j] = sum_k x[row i][k] C[4h+j][k]: lane j gets output 4h+j of the
+      // quad's rows; four accumulation chains (2 quads x 2 halves) interleaved
 #pragma unroll
-          for (int k = 0; k < B; ++k) acc[h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[k], cf[h][k], acc[h], 0, 0, 0);
+      for (int k = 0; k < B; ++k)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(xv[q][k], cf[h][k], acc[q][h], 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int o = 4 * h + j;
+        if (valid && o < B) {
+          float* dst = tile + 4 * pcol(col0 + o * s);
+          *reinterpret_cast<f32x4*>(dst) = acc[0][h];
+          *reinterpret_cast<f32x4*>(dst + plane) = acc[1][h];
         }
+      }
+    } else {
+      // D[i][j] = sum_k C[4h+i][k] x[row j][k]: lane j gets outputs 4h..4h+3 of row 4q+j
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const int o = 4 * h + j;
-          if (valid && o < B) *reinterpret_cast<f32x4*>(tile + qaddr(col0 + o * s, q)) = acc[h];
-        }
-      } else {
-        // D[i][j] = sum_k C[4h+i][k] x[row j][k]: lane j holds outputs 4h..4h+3 of row 4q+j
+      for (int k = 0; k < B; ++k)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-          for (int k = 0; k < B; ++k) acc[h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][k], xv[k], acc[h], 0, 0, 0);
-        }
+          for (int q = 0; q < 2; ++q)
+            acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][k], xv[q][k], acc[q][h], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
         const int r = 4 * q + j;
         if (valid && r < nr) {
-          float v[8] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w, acc[1].x, acc[1].y, acc[1].z, acc[1].w};
+          float v[8] = {acc[q][0].x, acc[q][0].y, acc[q][0].z, acc[q][0].w,
+                        acc[q][1].x, acc[q][1].y, acc[q][1].z, acc[q][1].w};
           T* y = static_cast<T*>(p.y) + (row0 + r) * p.ldy + col0;
           if constexpr (std::is_same<T, uint16_t>::value) {
             st_stream(y, pack_row<T>(v));
@@ -362,16 +390,18 @@ __global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) 
   int64_t tix = blockIdx.x;
   if (tix >= p.ntiles) return;   // uniform per workgroup
   if (io_wave) {
+    // data thread `it` owns chunks it, it + kIoThreads, ... of both row quads;
+    // the first kMaxIo of them (per quad) are prefetched into registers
     const int it = threadIdx.x - 64 * kCompWaves;
-    u32x4 w[kMaxIo][4];
-    // first tile: load and write
+    IoBlock pf[2][kMaxIo];
     {
       const int nr = tile_rows(p, tix);
-      for (int mb = it; mb < p.n_io; mb += kIoThreads) {
-        u32x4 one[4];
-        io_load<T>(p, tix * kRows, nr, mb, one);
-        io_to_lds<T>(p, tile, mb, one);
-      }
+      for (int q = 0; q < 2; ++q)
+        for (int c = it; c < p.chunks; c += kIoThreads) {
+          IoBlock one;
+          io_load<T>(p, tix * kRows, nr, q, c, one);
+          io_to_lds<T>(p, tile, q, c, one);
+        }
     }
     __syncthreads();
     for (; tix < p.ntiles; tix += gridDim.x) {
@@ -383,27 +413,33 @@ __global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) 
       // stream the next tile into registers while the stages run
       if (has_next) {
 #pragma unroll
-        for (int u = 0; u < kMaxIo; ++u) {
-          const int mb = it + u * kIoThreads;
-          if (mb < p.n_io) io_load<T>(p, nxt * kRows, nr_next, mb, w[u]);
-        }
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int u = 0; u < kMaxIo; ++u) {
+            const int c = it + u * kIoThreads;
+            if (c < p.chunks) io_load<T>(p, nxt * kRows, nr_next, q, c, pf[q][u]);
+          }
       }
       for (int t = 0; t < p.m; ++t) __syncthreads();
       if (!p.direct_out) {
-        for (int mb = it; mb < p.n_io; mb += kIoThreads) io_store<T>(p, tile, row0, nr, mb);
+        for (int q = 0; q < 2; ++q)
+          for (int c = it; c < p.chunks; c += kIoThreads) io_store<T>(p, tile, row0, nr, q, c);
         __syncthreads();
       }
       if (has_next) {
 #pragma unroll
-        for (int u = 0; u < kMaxIo; ++u) {
-          const int mb = it + u * kIoThreads;
-          if (mb < p.n_io) io_to_lds<T>(p, tile, mb, w[u]);
-        }
-        for (int mb = it + kMaxIo * kIoThreads; mb < p.n_io; mb += kIoThreads) {
-          u32x4 one[4];
-          io_load<T>(p, nxt * kRows, nr_next, mb, one);
-          io_to_lds<T>(p, tile, mb, one);
-        }
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int u = 0; u < kMaxIo; ++u) {
+            const int c = it + u * kIoThreads;
+            if (c < p.chunks) io_to_lds<T>(p, tile, q, c, pf[q][u]);
+          }
+        for (int q = 0; q < 2; ++q)
+          for (int c = it + kMaxIo * kIoThreads; c < p.chunks; c += kIoThreads) {
+            IoBlock one;
+            io_load<T>(p, nxt * kRows, nr_next, q, c, one);
+            io_to_lds<T>(p, tile, q, c, one);
+          }
       }
       __syncthreads();
     }
@@ -413,8 +449,7 @@ __global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) 
     float cf[2][8];
     {
       const int g0 = wave * 16 + (lane >> 2);
-      const int ng0 = p.d / p.st[0].b;
-      load_coef_any<TB, TR>(p, p.st[0], g0 < ng0 ? g0 : 0, lane & 3, g0 < ng0, cf);
+      load_coef_any<TB, TR>(p, p.st[0], g0 < p.st[0].G ? g0 : 0, lane & 3, g0 < p.st[0].G, cf);
     }
     __syncthreads();
     for (; tix < p.ntiles; tix += gridDim.x) {
@@ -455,8 +490,8 @@ hipError_t launch_mfma_roles(const MfmaParams& p, int grid, size_t lds, hipStrea
 
 template <typename T, typename TB>
 hipError_t launch_mfma_typed(const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
-  if (p.roles == 1) return launch_mfma_roles<T, TB, Roles<4, 4, 5>>(p, grid, lds, st);
-  return launch_mfma_roles<T, TB, Roles<8, 4, 2>>(p, grid, lds, st);
+  if (p.roles == 1) return launch_mfma_roles<T, TB, Roles<8, 4, 2>>(p, grid, lds, st);
+  return launch_mfma_roles<T, TB, Roles<8, 8, 1>>(p, grid, lds, st);
 }
 
 template <typename T>
@@ -471,17 +506,19 @@ hipError_t launch_mfma_blk(DT bdt, const MfmaParams& p, int grid, size_t lds, hi
 
 }  // namespace
 
-bool mfma_path_supported(const Plan& pl, DT io, const void* blocks, const void* x, int64_t ldx, const void* y,
-                         int64_t ldy) {
+bool mfma_path_supported(const Plan& pl, DT io, const void* blocks, const int8_t* signs, const void* x, int64_t ldx,
+                         const void* y, int64_t ldy) {
   if (io != DT::F32 && io != DT::BF16) return false;
   if (reinterpret_cast<uintptr_t>(blocks) % 16 != 0) return false;
   if (pl.d % 64 != 0 || pl.d > 5120) return false;
   for (int t = 0; t < pl.m; ++t) {
     const int b = pl.radix[t];
     if (b != 2 && b != 4 && b != 5 && b != 8) return false;
+    if ((pl.d / b) % 64 != 0) return false;
   }
   const int eb = io_bytes(io);
   if ((ldx * eb) % 16 || (ldy * eb) % 16) return false;
+  if (reinterpret_cast<uintptr_t>(signs) % 8 != 0) return false;
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16) return false;
   return true;
 }
@@ -500,9 +537,11 @@ hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, D
     StageFast& sf = p.st[i];
     sf.b = pl.radix[t];
     sf.s = (int)pl.stride[t];
+    sf.G = (int)(pl.d / sf.b);
     sf.blk_off = (int)pl.blk_off[t];
     sf.grp_off = (int)pl.grp_off[t];
     sf.div_s = (uint64_t)((1ull << 32) / (uint64_t)sf.s) + 1ull;
+    sf.div_b = (uint64_t)((1ull << 32) / (uint64_t)sf.b) + 1ull;
   }
   const StageFast& last = p.st[pl.m - 1];
   p.direct_out = (last.s == 1 && last.b == 8 && p.sign_mode != 2) ? 1 : 0;
@@ -517,7 +556,6 @@ hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, D
   p.ldy = ldy;
   p.rows = rows;
   p.roles = roles;
-  p.n_io = (kRows / 4) * p.chunks;
   p.ntiles = (rows + kRows - 1) / kRows;
   const size_t lds = (size_t)kRows * pl.d * sizeof(float);
   int64_t grid = cu_count_mfma();

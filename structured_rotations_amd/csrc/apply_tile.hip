@@ -189,7 +189,7 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
                              int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
                              int64_t rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (in_dt == out_dt && !env_flag("HARP_FORCE_GENERIC") && mfma_path_supported(pl, in_dt, blocks, x, ldx, y, ldy)) {
+  if (in_dt == out_dt && !env_flag("HARP_FORCE_GENERIC") && mfma_path_supported(pl, in_dt, blocks, signs, x, ldx, y, ldy)) {
     static const int roles = env_int("HARP_MFMA_ROLES", 0);
     return launch_apply_mfma(pl, inverse, blocks, bdt, scales, signs, x, ldx, in_dt, y, ldy, rows, roles, stream);
   }
