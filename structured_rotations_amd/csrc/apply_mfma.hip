@@ -29,14 +29,14 @@
 // outputs of one row; otherwise the data waves copy the finished tile out.
 #include <type_traits>
 
-#include "common.h"
-#include "kernels.h"
+#include "row_io.h"
 
 namespace harp {
 
 namespace {
 
-constexpr int kRows = 8;   // rows per tile (two row quads)
+using namespace rowk;
+
 
 // Wave roles: CW compute waves, IOW data waves, each data thread prefetching
 // up to MIO 16-byte chunks per row quad of the next tile into registers.
@@ -49,153 +49,11 @@ struct Roles {
   static constexpr int kGroupsPerRound = 16 * CW;
 };
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-struct StageFast {
-  int b;
-  int s;
-  int G;            // groups = d / b
-  int blk_off;
-  int grp_off;
-  uint64_t div_s;   // floor(2^32 / s) + 1: n / s == (n * div_s) >> 32 for n, s < 2^16
-  uint64_t div_b;
-};
-
-struct MfmaParams {
-  int d;
-  int m;
-  int transpose;
-  int sign_mode;     // 0 none, 1 on input, 2 on output
-  int chunks;        // 16-byte chunks per row
-  int direct_out;    // last stage stores straight to HBM
-  int roles;         // 0: 8 compute + 8 data waves; 1: 8 + 4
-  StageFast st[kMaxStagesDev];
-  const void* blocks;
-  const float* scales;
-  const int8_t* signs;
-  const void* x;
-  int64_t ldx;
-  void* y;
-  int64_t ldy;
-  int64_t rows;
-  int64_t ntiles;
-};
-
-__device__ __forceinline__ int fdiv(int n, uint64_t magic) { return (int)(((uint64_t)(uint32_t)n * magic) >> 32); }
-// LDS layout (one order for every stage, so each stage updates the tile in
-// place): two row-quad planes, plane q (rows 4q..4q+3) at q * 4d floats; in
-// a plane, column c's 4 rows form one 16-byte unit at unit index pcol(c).
-// pcol XORs bits 0..3 of c with bits 3..6 (bijective inside every 16
-// columns); for digit strides 512, 64, 8 and 1 the 4-byte gathers of a wave
-// hit every bank once.
-__device__ __forceinline__ int pcol(int c) { return c ^ ((c >> 3) & 15); }
-
-template <typename T> struct Io;
-template <> struct Io<uint16_t> { static constexpr int V = 8; };
-template <> struct Io<float> { static constexpr int V = 4; };
-
-__device__ __forceinline__ float sgnf(float v, uint32_t negbit) { return __uint_as_float(__float_as_uint(v) ^ negbit); }
-
-template <typename T>
-__device__ __forceinline__ float elem(const u32x4& w, int u);
-template <>
-__device__ __forceinline__ float elem<uint16_t>(const u32x4& w, int u) {
-  const uint32_t word = u < 2 ? w.x : (u < 4 ? w.y : (u < 6 ? w.z : w.w));
-  return (u & 1) ? bf16_hi(word) : bf16_lo(word);
-}
-template <>
-__device__ __forceinline__ float elem<float>(const u32x4& w, int u) {
-  return __uint_as_float(u == 0 ? w.x : (u == 1 ? w.y : (u == 2 ? w.z : w.w)));
-}
-
-template <typename T>
-__device__ __forceinline__ u32x4 pack_row(const float* v);
-template <>
-__device__ __forceinline__ u32x4 pack_row<uint16_t>(const float* v) {
-  return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-}
-template <>
-__device__ __forceinline__ u32x4 pack_row<float>(const float* v) {
-  return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-}
-
-// ---------------------------------------------------------------- data waves
-// Micro-block mb = (row quad q, 16-byte chunk c): rows 4q..4q+3 x V columns,
-// plus the V sign bytes of those columns (zero = no flip).
-struct IoBlock {
-  u32x4 w[4];
-  uint2 sg;
-};
-
-template <typename T>
-__device__ __forceinline__ void io_load(const MfmaParams& p, int64_t row0, int nr, int q, int c, IoBlock& blk) {
-  constexpr int V = Io<T>::V;
-  const T* x = static_cast<const T*>(p.x);
-  // rows past the end of a ragged last tile re-read the last row: they are
-  // transformed like the others but never stored
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * q + i < nr ? 4 * q + i : nr - 1;
-    blk.w[i] = ld_stream(x + (row0 + r) * p.ldx + (int64_t)c * V);
-  }
-  blk.sg = uint2{0u, 0u};
-  if (p.sign_mode == 1) {
-    const int8_t* sp = p.signs + c * V;
-    if constexpr (V == 8) blk.sg = *reinterpret_cast<const uint2*>(sp);
-    else blk.sg.x = *reinterpret_cast<const uint32_t*>(sp);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ f32x4 io_column(const IoBlock& blk, int u) {
-  // sign byte u (0x01 or 0xff): bit 7 set for -1
-  const uint32_t neg = (((u < 4 ? blk.sg.x : blk.sg.y) >> (8 * (u & 3))) & 0x80u) << 24;
-  f32x4 v;
-  v.x = sgnf(elem<T>(blk.w[0], u), neg); v.y = sgnf(elem<T>(blk.w[1], u), neg);
-  v.z = sgnf(elem<T>(blk.w[2], u), neg); v.w = sgnf(elem<T>(blk.w[3], u), neg);
-  return v;
-}
-
-// Writes a micro-block (rows 4q..4q+3 of the V columns of chunk c).  The
-// chunk's columns c*V + u share bits 3..6 (V <= 8 and chunks are aligned), so
-// their units are (c*V ^ m) ^ u with one mask m.
-template <typename T>
-__device__ __forceinline__ void io_to_lds(const MfmaParams& p, float* tile, int q, int c, const IoBlock& blk) {
-  constexpr int V = Io<T>::V;
-  float* plane = tile + q * 4 * p.d;
-  const int base = pcol(c * V);
-#pragma unroll
-  for (int u = 0; u < V; ++u)
-    *reinterpret_cast<f32x4*>(plane + 4 * (base ^ u)) = io_column<T>(blk, u);
-}
-
-template <typename T>
-__device__ __forceinline__ void io_store(const MfmaParams& p, const float* tile, int64_t row0, int nr, int q, int c) {
-  constexpr int V = Io<T>::V;
-  T* y = static_cast<T*>(p.y);
-  const float* plane = tile + q * 4 * p.d;
-  float v[4][V];
-#pragma unroll
-  for (int u = 0; u < V; ++u) {
-    const int col = c * V + u;
-    f32x4 t = *reinterpret_cast<const f32x4*>(plane + 4 * pcol(col));
-    if (p.sign_mode == 2 && p.signs[col] < 0) {
-      t.x = -t.x; t.y = -t.y; t.z = -t.z; t.w = -t.w;
-    }
-    v[0][u] = t.x; v[1][u] = t.y; v[2][u] = t.z; v[3][u] = t.w;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * q + i;
-    if (r < nr) st_stream(y + (row0 + r) * p.ldy + (int64_t)c * V, pack_row<T>(v[i]));
-  }
-}
-
 // ---------------------------------------------------------------- coefficients
 // cf[h][k] = C[4h + j][k] of group g (C = B forward, B^T inverse); zero
 // outside the radix or for an idle lane.
 template <int B, typename TB, bool TR>
-__device__ __forceinline__ void load_coef(const MfmaParams& p, const StageFast& sd, int g, int j, bool valid,
+__device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g, int j, bool valid,
                                           float (&cf)[2][8]) {
   const TB* blk = static_cast<const TB*>(p.blocks) + sd.blk_off + (int64_t)g * B * B;
   float scale = 1.0f;
@@ -253,7 +111,7 @@ __device__ __forceinline__ void load_coef(const MfmaParams& p, const StageFast& 
 }
 
 template <typename TB, bool TR>
-__device__ __forceinline__ void load_coef_any(const MfmaParams& p, const StageFast& sd, int g, int j, bool valid,
+__device__ __forceinline__ void load_coef_any(const RowParams& p, const StageFast& sd, int g, int j, bool valid,
                                               float (&cf)[2][8]) {
   switch (sd.b) {
     case 2: load_coef<2, TB, TR>(p, sd, g, j, valid, cf); break;
@@ -267,7 +125,7 @@ __device__ __forceinline__ void load_coef_any(const MfmaParams& p, const StageFa
 // One stage over the tile.  cf holds round 0's coefficients on entry and the
 // next stage's (or, after the last stage, the next tile's first) on exit.
 template <int B, typename T, typename TB, bool TR, bool DIRECT, int GPR>
-__device__ void mfma_stage(const MfmaParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
+__device__ void mfma_stage(const RowParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
   constexpr int NH = B > 4 ? 2 : 1;
   const StageFast& sd = p.st[t];
   const int lane = threadIdx.x & 63;
@@ -361,7 +219,7 @@ __device__ void mfma_stage(const MfmaParams& p, int t, float* tile, float (&cf)[
 }
 
 template <typename T, typename TB, bool TR, int GPR>
-__device__ void run_stage(const MfmaParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
+__device__ void run_stage(const RowParams& p, int t, float* tile, float (&cf)[2][8], int64_t row0, int nr) {
   if (p.direct_out && t == p.m - 1) {
     mfma_stage<8, T, TB, TR, true, GPR>(p, t, tile, cf, row0, nr);
     return;
@@ -375,13 +233,9 @@ __device__ void run_stage(const MfmaParams& p, int t, float* tile, float (&cf)[2
   }
 }
 
-__device__ __forceinline__ int tile_rows(const MfmaParams& p, int64_t tix) {
-  const int64_t left = p.rows - tix * kRows;
-  return left < kRows ? (int)left : kRows;
-}
 
 template <typename T, typename TB, bool TR, typename RL>
-__global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) {
+__global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(RowParams p) {
   constexpr int kCompWaves = RL::kCompWaves;
   constexpr int kIoThreads = RL::kIoThreads;
   constexpr int kMaxIo = RL::kMaxIo;
@@ -390,60 +244,10 @@ __global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) 
   int64_t tix = blockIdx.x;
   if (tix >= p.ntiles) return;   // uniform per workgroup
   if (io_wave) {
-    // data thread `it` owns chunks it, it + kIoThreads, ... of both row quads;
-    // the first kMaxIo of them (per quad) are prefetched into registers
-    const int it = threadIdx.x - 64 * kCompWaves;
-    IoBlock pf[2][kMaxIo];
-    {
-      const int nr = tile_rows(p, tix);
-      for (int q = 0; q < 2; ++q)
-        for (int c = it; c < p.chunks; c += kIoThreads) {
-          IoBlock one;
-          io_load<T>(p, tix * kRows, nr, q, c, one);
-          io_to_lds<T>(p, tile, q, c, one);
-        }
-    }
-    __syncthreads();
-    for (; tix < p.ntiles; tix += gridDim.x) {
-      const int64_t row0 = tix * kRows;
-      const int nr = tile_rows(p, tix);
-      const int64_t nxt = tix + gridDim.x;
-      const bool has_next = nxt < p.ntiles;
-      const int nr_next = has_next ? tile_rows(p, nxt) : 0;
-      // stream the next tile into registers while the stages run
-      if (has_next) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int u = 0; u < kMaxIo; ++u) {
-            const int c = it + u * kIoThreads;
-            if (c < p.chunks) io_load<T>(p, nxt * kRows, nr_next, q, c, pf[q][u]);
-          }
-      }
-      for (int t = 0; t < p.m; ++t) __syncthreads();
-      if (!p.direct_out) {
-        for (int q = 0; q < 2; ++q)
-          for (int c = it; c < p.chunks; c += kIoThreads) io_store<T>(p, tile, row0, nr, q, c);
-        __syncthreads();
-      }
-      if (has_next) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int u = 0; u < kMaxIo; ++u) {
-            const int c = it + u * kIoThreads;
-            if (c < p.chunks) io_to_lds<T>(p, tile, q, c, pf[q][u]);
-          }
-        for (int q = 0; q < 2; ++q)
-          for (int c = it + kMaxIo * kIoThreads; c < p.chunks; c += kIoThreads) {
-            IoBlock one;
-            io_load<T>(p, nxt * kRows, nr_next, q, c, one);
-            io_to_lds<T>(p, tile, q, c, one);
-          }
-      }
-      __syncthreads();
-    }
-  } else {
+    data_waves<T, kIoThreads, kMaxIo>(p, tile, threadIdx.x - 64 * kCompWaves);
+    return;
+  }
+  {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float cf[2][8];
@@ -465,21 +269,8 @@ __global__ void __launch_bounds__(RL::kThreads) apply_mfma_kernel(MfmaParams p) 
   }
 }
 
-int cu_count_mfma() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      return 256;
-  }
-  return cus;
-}
-
 template <typename T, typename TB, typename RL>
-hipError_t launch_mfma_roles(const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_mfma_roles(const RowParams& p, int grid, size_t lds, hipStream_t st) {
   auto kern = p.transpose ? apply_mfma_kernel<T, TB, true, RL> : apply_mfma_kernel<T, TB, false, RL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -489,24 +280,24 @@ hipError_t launch_mfma_roles(const MfmaParams& p, int grid, size_t lds, hipStrea
 }
 
 template <typename T, typename TB>
-hipError_t launch_mfma_typed(const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
-  if (p.roles == 1) return launch_mfma_roles<T, TB, Roles<8, 4, 2>>(p, grid, lds, st);
+hipError_t launch_mfma_typed(const RowParams& p, int roles, int grid, size_t lds, hipStream_t st) {
+  if (roles == 1) return launch_mfma_roles<T, TB, Roles<8, 4, 2>>(p, grid, lds, st);
   return launch_mfma_roles<T, TB, Roles<8, 8, 1>>(p, grid, lds, st);
 }
 
 template <typename T>
-hipError_t launch_mfma_blk(DT bdt, const MfmaParams& p, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_mfma_blk(DT bdt, const RowParams& p, int roles, int grid, size_t lds, hipStream_t st) {
   switch (bdt) {
-    case DT::F32: return launch_mfma_typed<T, float>(p, grid, lds, st);
-    case DT::BF16: return launch_mfma_typed<T, uint16_t>(p, grid, lds, st);
-    case DT::I8: return launch_mfma_typed<T, int8_t>(p, grid, lds, st);
+    case DT::F32: return launch_mfma_typed<T, float>(p, roles, grid, lds, st);
+    case DT::BF16: return launch_mfma_typed<T, uint16_t>(p, roles, grid, lds, st);
+    case DT::I8: return launch_mfma_typed<T, int8_t>(p, roles, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-bool mfma_path_supported(const Plan& pl, DT io, const void* blocks, const int8_t* signs, const void* x, int64_t ldx,
+bool row_path_supported(const Plan& pl, DT io, const void* blocks, const int8_t* signs, const void* x, int64_t ldx,
                          const void* y, int64_t ldy) {
   if (io != DT::F32 && io != DT::BF16) return false;
   if (reinterpret_cast<uintptr_t>(blocks) % 16 != 0) return false;
@@ -527,41 +318,12 @@ hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, D
                              const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
                              int64_t rows, int roles, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  MfmaParams p{};
-  p.d = (int)pl.d;
-  p.m = pl.m;
-  p.transpose = inverse ? 1 : 0;
-  p.sign_mode = signs ? (inverse ? 2 : 1) : 0;
-  for (int i = 0; i < pl.m; ++i) {
-    const int t = inverse ? pl.m - 1 - i : i;
-    StageFast& sf = p.st[i];
-    sf.b = pl.radix[t];
-    sf.s = (int)pl.stride[t];
-    sf.G = (int)(pl.d / sf.b);
-    sf.blk_off = (int)pl.blk_off[t];
-    sf.grp_off = (int)pl.grp_off[t];
-    sf.div_s = (uint64_t)((1ull << 32) / (uint64_t)sf.s) + 1ull;
-    sf.div_b = (uint64_t)((1ull << 32) / (uint64_t)sf.b) + 1ull;
-  }
-  const StageFast& last = p.st[pl.m - 1];
-  p.direct_out = (last.s == 1 && last.b == 8 && p.sign_mode != 2) ? 1 : 0;
-  const int V = io == DT::BF16 ? 8 : 4;
-  p.chunks = (int)(pl.d / V);
-  p.blocks = blocks;
-  p.scales = scales;
-  p.signs = signs;
-  p.x = x;
-  p.ldx = ldx;
-  p.y = y;
-  p.ldy = ldy;
-  p.rows = rows;
-  p.roles = roles;
-  p.ntiles = (rows + kRows - 1) / kRows;
+  RowParams p = make_row_params(pl, inverse, blocks, scales, signs, x, ldx, io, y, ldy, rows);
   const size_t lds = (size_t)kRows * pl.d * sizeof(float);
-  int64_t grid = cu_count_mfma();
+  int64_t grid = cu_count();
   if (grid > p.ntiles) grid = p.ntiles;
-  if (io == DT::BF16) return launch_mfma_blk<uint16_t>(bdt, p, (int)grid, lds, stream);
-  return launch_mfma_blk<float>(bdt, p, (int)grid, lds, stream);
+  if (io == DT::BF16) return launch_mfma_blk<uint16_t>(bdt, p, roles, (int)grid, lds, stream);
+  return launch_mfma_blk<float>(bdt, p, roles, (int)grid, lds, stream);
 }
 
 }  // namespace harp

@@ -9,6 +9,9 @@
 namespace harp {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Per-stage descriptor in processing order (already reversed for inverses).
 struct StageDesc {
@@ -33,6 +36,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+// Same rounding (nearest, ties to even) through gfx950's packed conversion
+// instruction, one VALU op for two values.
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  const bf16x2_t h = __builtin_convertvector(f32x2{lo, hi}, bf16x2_t);
+  uint32_t w;
+  __builtin_memcpy(&w, &h, 4);
+  return w;
 }
 
 // fp64 -> bfloat16 bits, round to nearest, ties to even, directly from the

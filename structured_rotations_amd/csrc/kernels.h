@@ -22,11 +22,14 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
                              int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
                              int64_t rows, hipStream_t stream);
 
-// Matrix-core row kernel (radices <= 8, d % 64 == 0, d <= 5120, 16-byte
-// aligned rows and blocks, same I/O dtype on both sides).  roles selects the
-// wave split (0: 8 compute + 4 data waves, 1: 4 + 4).
-bool mfma_path_supported(const Plan& pl, DT io, const void* blocks, const int8_t* signs, const void* x, int64_t ldx,
-                         const void* y, int64_t ldy);
+// Row-tile kernels (radices 2, 4, 5, 8; d % 64 == 0, d <= 5120; 16-byte
+// aligned rows and blocks; same I/O dtype on both sides): the vector-ALU
+// kernel and the matrix-core kernel.  roles selects the wave split.
+bool row_path_supported(const Plan& pl, DT io, const void* blocks, const int8_t* signs, const void* x, int64_t ldx,
+                        const void* y, int64_t ldy);
+hipError_t launch_apply_valu(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
+                             const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
+                             int64_t rows, int roles, hipStream_t stream);
 hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
                              const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
                              int64_t rows, int roles, hipStream_t stream);

@@ -218,6 +218,49 @@ def test_rht_fp32_schedules(sch):
     assert_rows_close(from_dev(y), O.rht_compose(x.astype(float), signs.astype(float)), 1e-5, f"rht {sch}")
 
 
+@pytest.mark.parametrize("d", [4096, 8192])
+@pytest.mark.parametrize("k", [1, 2, 3, 8])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rht_wave_path(d, k, io):
+    # d = 4096 / 8192 with 16-byte aligned rows run the wave-per-row kernel:
+    # odd and even k end in different register layouts; k = 8 is the maximum;
+    # 37 rows leave most waves of the last sweep idle; rows are strided.
+    sch = (8, 8, 8, 8) if d == 4096 else (8, 8, 8, 16)
+    rng = np.random.default_rng(100 * k + d // 1024)
+    signs = np.where(rng.integers(0, 2, (k, d)) == 1, 1, -1).astype(np.int8)
+    x = W.round_io(rng.standard_t(3, size=(37, d)).astype(np.float32), io)
+    tol = 1e-5 if io == "f32" else TOL["bf16"]
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    ld = d + 64
+    xs = torch.zeros(37, ld, dtype=dt, device="cuda")
+    xs[:, :d] = to_dev(x, io)
+    sg = signs_dev(signs)
+    y = api.rht_compose(sch, d, sg, xs[:, :d])
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(y), O.rht_compose(x.astype(np.float64), signs.astype(float)), tol, f"rht d={d} k={k}")
+    yin = from_dev(y)
+    xr = api.rht_compose(sch, d, sg, y, inverse=True)
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(xr), O.rht_compose(yin, signs.astype(float), inverse=True), tol, "rht inverse")
+
+
+def test_rht_wave_matches_tile_path():
+    # an odd leading dimension (bf16, 2-byte aligned rows) takes the LDS tile
+    # kernel; both paths compute the same H_d D_k ... H_d D_1 x
+    sch, d, k = (8, 8, 8, 16), 8192, 3
+    rng = np.random.default_rng(77)
+    signs = np.where(rng.integers(0, 2, (k, d)) == 1, 1, -1).astype(np.int8)
+    x = W.round_io(rng.standard_normal((9, d)).astype(np.float32), "bf16")
+    xs = torch.zeros(9, d + 1, dtype=torch.bfloat16, device="cuda")
+    xs[:, :d] = to_dev(x, "bf16")
+    y_tile = api.rht_compose(sch, d, signs_dev(signs), xs[:, :d])
+    y_wave = api.rht_compose(sch, d, signs_dev(signs), to_dev(x, "bf16"))
+    torch.cuda.synchronize()
+    ref = O.rht_compose(x.astype(np.float64), signs.astype(float))
+    assert_rows_close(from_dev(y_tile), ref, TOL["bf16"], "tile path")
+    assert_rows_close(from_dev(y_wave), ref, TOL["bf16"], "wave path")
+
+
 # ------------------------------------------------------------------ two-sided rotation
 def _two_sided_small():
     rng = np.random.default_rng(31)
