@@ -17,7 +17,6 @@ cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,17 +29,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["structured_rotations_amd/csrc/" + f for f in
-                  ("apply_tile.hip", "tile_io.h", "common.h", "rht.hip", "rotate_cols.hip")]
 
 
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        p = os.path.join(ROOT, f)
-        if os.path.exists(p):
-            h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
+    from structured_rotations_amd.build import source_hash
+    return source_hash()
 
 
 def traffic_from_profile(workload: str, blk: str):
@@ -113,6 +106,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of the batch instead (counter calibration)")
+    ap.add_argument("--flush", action="store_true",
+                    help="per-launch timing with L2 and MALL flushed (a 1 GiB write) before every launch")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the apply path has no cross-GPU step and this build runs on a "
@@ -190,6 +185,19 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    flushed = None
+    if args.flush:
+        # same launches, each after a 1 GiB write that evicts L2 and the MALL
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in evf:
+            scratch.fill_(1.0)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        flushed = np.array([a.elapsed_time(b) for a, b in evf])
+        del scratch
     ms_per_step = total_ms / args.steps
     kern_ms = float(per_launch.mean())
     value = units / (ms_per_step * 1e-3)
@@ -218,7 +226,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-io/f32-compute" if io == "bf16" else "f32",
+        "dtype": "f32",
         "data": "synthetic (seeded Student-t nu=3 rows with outlier channels; random Cayley/Givens parameters)",
         "config": {"workload": args.workload if not args.copy_calibration else "device copy of " + args.workload,
                    "rows": rows, "d": d, "schedule": list(sch), "io": io, "blocks": args.blk,
@@ -230,6 +238,7 @@ def main() -> int:
         "kernel_ms_p10_p90": [round(float(np.percentile(per_launch, 10)), 5),
                               round(float(np.percentile(per_launch, 90)), 5)],
         "alg_bytes_per_launch": alg_bytes,
+        "kernel_ms_mean_flushed": None if flushed is None else round(float(flushed.mean()), 5),
         "wall_s_timed": round(wall, 4),
         "parity_max_row_rel_l2": parity,
     }
