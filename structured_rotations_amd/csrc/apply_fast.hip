@@ -1,0 +1,531 @@
+// Schedule-specialised matrix-core row kernel for the HARP transform.
+//
+// HARP technical summary (gist.science 2605.29843), §2.1/§2.2: stage t
+// applies, to every group of coordinates that agree on all digits but digit
+// t, its own b_t x b_t orthogonal block.  This kernel computes exactly what
+// the generic matrix-core kernel computes (same 8-row tile, same
+// v_mfma_f32_4x4x1f32 mapping: a block of 4 lanes owns one group, lane j
+// supplies row j's input and coefficient row 4h+j), but for schedules known
+// at compile time, so that the per-round work is almost only matrix-core
+// instructions and LDS accesses:
+//   * every stage's radix and digit stride are constants: group -> column
+//     arithmetic folds, and the next stage's coefficient load needs no
+//     radix dispatch;
+//   * with the padded layout (one spare unit per 8 columns) the B inputs of
+//     a group sit at base + constant(k), so each round computes one LDS
+//     address and the rest are immediate offsets (checked at compile time);
+//   * coefficient registers alternate between two buffers from round to
+//     round (loaded one round ahead, into the buffer the previous round has
+//     finished with) instead of being copied;
+//   * coefficient loads are unconditional (rows past the radix re-read the
+//     last row; those outputs are never written), so nothing is zero-filled.
+// Data waves, signs and the direct store of a contiguous last stage are as
+// in the generic kernel.
+#include <type_traits>
+
+#include "row_io.h"
+
+namespace harp {
+
+namespace {
+
+using namespace rowk;
+
+constexpr int kCW = 8;                    // compute waves
+constexpr int kIOW = 8;                   // data waves
+constexpr int kGPR = 16 * kCW;            // groups per round
+constexpr int kThreads = 64 * (kCW + kIOW);
+
+template <int B_, int S_>
+struct St {
+  static constexpr int B = B_;
+  static constexpr int S = S_;
+};
+
+template <class... Ss>
+struct List {
+  static constexpr int size = sizeof...(Ss);
+};
+template <int I, class L>
+struct At;
+template <class H, class... T>
+struct At<0, List<H, T...>> {
+  using type = H;
+};
+template <int I, class H, class... T>
+struct At<I, List<H, T...>> {
+  using type = typename At<I - 1, List<T...>>::type;
+};
+
+// D: row length; Lay: LDS unit layout; L: stages in processing order.
+template <int D_, class Lay_, class L_>
+struct Sched {
+  static constexpr int D = D_;
+  using Lay = Lay_;
+  using L = L_;
+  static constexpr int M = L::size;
+};
+
+template <int B, int S>
+__host__ __device__ constexpr int col0_of(int g) {
+  return (g / S) * (B - 1) * S + g;
+}
+
+// True when, for every group of the stage, the units of its B columns are
+// unit(col0) + (unit(k S) - unit(0)): then one address per group suffices.
+template <class Lay, int D, int B, int S>
+constexpr bool linear_stage() {
+  for (int g = 0; g < D / B; ++g) {
+    const int c0 = col0_of<B, S>(g);
+    for (int k = 0; k < B; ++k)
+      if (Lay::unit(c0 + k * S) - Lay::unit(c0) != Lay::unit(k * S) - Lay::unit(0)) return false;
+  }
+  return true;
+}
+
+template <class Sch, int I>
+constexpr int rounds_before() {
+  if constexpr (I == 0) {
+    return 0;
+  } else {
+    using Sp = typename At<I - 1, typename Sch::L>::type;
+    return rounds_before<Sch, I - 1>() + Sch::D / Sp::B / kGPR;
+  }
+}
+
+template <class Sch, int I = 0>
+constexpr int rounds_before_rt(int t) {
+  if constexpr (I >= Sch::M) {
+    return 0;
+  } else {
+    using Si = typename At<I, typename Sch::L>::type;
+    return I < t ? Sch::D / Si::B / kGPR + rounds_before_rt<Sch, I + 1>(t) : 0;
+  }
+}
+
+// cf[h][k] = C[4h + j][k] of group g (C = B forward, B^T inverse); lanes whose
+// row 4h + j is past the radix re-read row B - 1 (their outputs are dropped).
+template <int B, typename TB, bool TR>
+__device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g, int j, float (&cf)[2][8]) {
+  const TB* blk = static_cast<const TB*>(p.blocks) + sd.blk_off + (int64_t)g * B * B;
+  constexpr int NH = B > 4 ? 2 : 1;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int o = 4 * h + j < B ? 4 * h + j : B - 1;
+    if constexpr (!TR && (B == 8 || B == 4)) {
+      const TB* row = blk + o * B;
+      if constexpr (std::is_same<TB, float>::value) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(row);
+        cf[h][0] = __uint_as_float(a.x); cf[h][1] = __uint_as_float(a.y);
+        cf[h][2] = __uint_as_float(a.z); cf[h][3] = __uint_as_float(a.w);
+        if constexpr (B == 8) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(row + 4);
+          cf[h][4] = __uint_as_float(b.x); cf[h][5] = __uint_as_float(b.y);
+          cf[h][6] = __uint_as_float(b.z); cf[h][7] = __uint_as_float(b.w);
+        }
+      } else if constexpr (B == 8) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(row);
+        cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
+        cf[h][4] = bf16_lo(a.z); cf[h][5] = bf16_hi(a.z); cf[h][6] = bf16_lo(a.w); cf[h][7] = bf16_hi(a.w);
+      } else {
+        const uint2 a = *reinterpret_cast<const uint2*>(row);
+        cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < B; ++k) cf[h][k] = coef<TB>(blk, TR ? k * B + o : o * B + k, 1.0f);
+    }
+  }
+}
+
+// One round: 16 groups per compute wave, both row quads.
+template <class Sch, int B, int S, bool TR, bool DIRECT, typename T>
+__device__ __forceinline__ void round_compute(const RowParams& p, float* tile, int g, const float (&cf)[2][8],
+                                              int64_t row0, int nr, int j) {
+  using Lay = typename Sch::Lay;
+  constexpr int D = Sch::D;
+  constexpr int NH = B > 4 ? 2 : 1;
+  constexpr int PLANE = 4 * Lay::units(D);
+  constexpr bool LIN = linear_stage<Lay, D, B, S>();
+  const int col0 = col0_of<B, S>(g);
+  float xv[2][B];
+  const float* src = tile + 4 * Lay::unit(col0) + j;
+#pragma unroll
+  for (int k = 0; k < B; ++k) {
+    const int a = LIN ? 4 * (Lay::unit(k * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + k * S) - 4 * Lay::unit(col0);
+    xv[0][k] = src[a];
+    xv[1][k] = src[a + PLANE];
+  }
+  // D[i][j] = sum_k C[4h+i][k] x[row 4q+j][k]: lane j ends with outputs
+  // 4h..4h+3 of row 4q+j.  Written back as 4-byte stores (output 4h+i of the
+  // four rows of a quad lands in one 16-byte unit, filled by the block's four
+  // lanes), which keeps every store free of bank conflicts; for a contiguous
+  // radix-8 last stage the 8 outputs are 8 consecutive columns of one row and
+  // go straight to HBM.
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int k = 1; k < B; ++k)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][k], xv[q][k], acc[q][h], 0, 0, 0);
+  if constexpr (!DIRECT) {
+    float* dst = tile + 4 * Lay::unit(col0) + j;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 4 * h + i;
+        if (o < B) {
+          const int a = LIN ? 4 * (Lay::unit(o * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + o * S) - 4 * Lay::unit(col0);
+          dst[a] = acc[0][h][i];
+          dst[a + PLANE] = acc[1][h][i];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 4 * q + j;
+      if (r < nr) {
+        float v[8] = {acc[q][0].x, acc[q][0].y, acc[q][0].z, acc[q][0].w,
+                      acc[q][1].x, acc[q][1].y, acc[q][1].z, acc[q][1].w};
+        T* y = static_cast<T*>(p.y) + (row0 + r) * p.ldy + col0;
+        if constexpr (std::is_same<T, uint16_t>::value) {
+          st_stream(y, u32x4{pack_bf16x2_hw(v[0], v[1]), pack_bf16x2_hw(v[2], v[3]), pack_bf16x2_hw(v[4], v[5]),
+                             pack_bf16x2_hw(v[6], v[7])});
+        } else {
+          st_stream(y, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+          st_stream(y + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+        }
+      }
+    }
+  }
+}
+
+// Stage I of the schedule over the tile.  SW selects which coefficient buffer
+// holds round 0 (loaded by the previous stage); on exit the next stage's round
+// 0 (after the last stage: the next tile's) is in the buffer the next stage
+// expects, which is compile-time known from the round counts.
+template <class Sch, int I, bool SW, bool TR, bool DOUT, typename T, typename TB>
+__device__ __forceinline__ void run_stage(const RowParams& p, float* tile, float (&ca)[2][8], float (&cb)[2][8], int gb,
+                                          int j, int64_t row0, int nr) {
+  constexpr int M = Sch::M;
+  using Sg = typename At<I, typename Sch::L>::type;
+  using Sn = typename At<(I + 1) % M, typename Sch::L>::type;
+  constexpr int B = Sg::B, S = Sg::S, R = Sch::D / B / kGPR;
+  constexpr bool DIRECT = DOUT && I == M - 1;
+  static_assert(!DIRECT || (B == 8 && S == 1), "direct store needs a contiguous radix-8 last stage");
+  float(&X)[2][8] = SW ? cb : ca;
+  float(&Y)[2][8] = SW ? ca : cb;
+  const StageFast& sd = p.st[I];
+  const StageFast& sn = p.st[(I + 1) % M];
+  if constexpr (R % 2 == 0) {
+#pragma unroll 1
+    for (int r = 0; r < R - 2; r += 2) {
+      load_coef<B, TB, TR>(p, sd, (r + 1) * kGPR + gb, j, Y);
+      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, r * kGPR + gb, X, row0, nr, j);
+      load_coef<B, TB, TR>(p, sd, (r + 2) * kGPR + gb, j, X);
+      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (r + 1) * kGPR + gb, Y, row0, nr, j);
+    }
+    load_coef<B, TB, TR>(p, sd, (R - 1) * kGPR + gb, j, Y);
+    round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 2) * kGPR + gb, X, row0, nr, j);
+    load_coef<Sn::B, TB, TR>(p, sn, gb, j, X);
+    round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 1) * kGPR + gb, Y, row0, nr, j);
+  } else {
+#pragma unroll 1
+    for (int r = 0; r < R - 1; r += 2) {
+      load_coef<B, TB, TR>(p, sd, (r + 1) * kGPR + gb, j, Y);
+      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, r * kGPR + gb, X, row0, nr, j);
+      load_coef<B, TB, TR>(p, sd, (r + 2) * kGPR + gb, j, X);
+      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (r + 1) * kGPR + gb, Y, row0, nr, j);
+    }
+    load_coef<Sn::B, TB, TR>(p, sn, gb, j, Y);
+    round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 1) * kGPR + gb, X, row0, nr, j);
+  }
+  __syncthreads();
+  if constexpr (I + 1 < M) {
+    constexpr bool SW2 = (R % 2 == 0) ? SW : !SW;
+    run_stage<Sch, I + 1, SW2, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, row0, nr);
+  }
+}
+
+template <class Sch, bool SW, bool TR, bool DOUT, typename T, typename TB>
+__device__ __forceinline__ void tile_body(const RowParams& p, float* tile, float (&ca)[2][8], float (&cb)[2][8],
+                                          int gb, int j, int64_t tix) {
+  const int64_t row0 = tix * kRows;
+  const int nr = tile_rows(p, tix);
+  run_stage<Sch, 0, SW, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, row0, nr);
+  if (!DOUT) __syncthreads();   // data waves copy the tile out
+  __syncthreads();              // data waves write the next tile in
+}
+
+template <class Sch, bool TR, bool DOUT, typename T, typename TB>
+__global__ void __launch_bounds__(kThreads) apply_fast_kernel(RowParams p) {
+  constexpr int RT = rounds_before<Sch, Sch::M>();   // rounds per tile
+  extern __shared__ float tile[];
+  int64_t tix = blockIdx.x;
+  if (tix >= p.ntiles) return;   // uniform per workgroup
+  if (threadIdx.x >= 64 * kCW) {
+    data_waves<T, 64 * kIOW, 1, typename Sch::Lay>(p, tile, threadIdx.x - 64 * kCW);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int gb = wave * 16 + (lane >> 2);
+  const int j = lane & 3;
+  float ca[2][8], cb[2][8];
+  using S0 = typename At<0, typename Sch::L>::type;
+  load_coef<S0::B, TB, TR>(p, p.st[0], gb, j, ca);
+  __syncthreads();
+  while (true) {
+    tile_body<Sch, false, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, tix);
+    tix += gridDim.x;
+    if (tix >= p.ntiles) break;
+    if constexpr (RT % 2 == 1) {
+      // an odd number of rounds per tile leaves the next tile's first
+      // coefficients in the other buffer
+      tile_body<Sch, true, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, tix);
+      tix += gridDim.x;
+      if (tix >= p.ntiles) break;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Pipelined variant for schedules whose tile takes a number of rounds
+// divisible by 4 (d = 4096, (8,8,8,8): 16 rounds).  Every round of a tile is
+// unrolled, so the coefficient buffers rotate at compile time: round n uses
+// buffer n % 4 and prefetches round n + 3 (possibly of the next tile) into
+// buffer (n + 3) % 4, three rounds of latency instead of one.  Inside a
+// stage the next round's LDS inputs are read while this round's products
+// run.  8 compute waves + 4 data waves (three waves per SIMD) leave room for
+// the extra buffers.
+constexpr int kPCW = 8;
+constexpr int kPIOW = 4;
+constexpr int kPThreads = 64 * (kPCW + kPIOW);
+static_assert(kPCW == kCW, "the round size kGPR assumes 8 compute waves");
+
+template <class Sch, int N>
+constexpr int stage_of() {
+  int t = 0;
+  while (t + 1 < Sch::M && N >= rounds_before_rt<Sch>(t + 1)) ++t;
+  return t;
+}
+
+template <class Sch, int B, int S>
+__device__ __forceinline__ void read_inputs(const float* tile, int g, int j, float (&xv)[2][8]) {
+  using Lay = typename Sch::Lay;
+  constexpr int PLANE = 4 * Lay::units(Sch::D);
+  constexpr bool LIN = linear_stage<Lay, Sch::D, B, S>();
+  const int col0 = col0_of<B, S>(g);
+  const float* src = tile + 4 * Lay::unit(col0) + j;
+#pragma unroll
+  for (int k = 0; k < B; ++k) {
+    const int a = LIN ? 4 * (Lay::unit(k * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + k * S) - 4 * Lay::unit(col0);
+    xv[0][k] = src[a];
+    xv[1][k] = src[a + PLANE];
+  }
+}
+
+template <class Sch, int B, int S, bool DIRECT, typename T>
+__device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, const float (&cf)[2][8],
+                                               const float (&xv)[2][8], int64_t row0, int nr, int j) {
+  using Lay = typename Sch::Lay;
+  constexpr int NH = B > 4 ? 2 : 1;
+  constexpr int PLANE = 4 * Lay::units(Sch::D);
+  constexpr bool LIN = linear_stage<Lay, Sch::D, B, S>();
+  const int col0 = col0_of<B, S>(g);
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int k = 1; k < B; ++k)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][k], xv[q][k], acc[q][h], 0, 0, 0);
+  if constexpr (!DIRECT) {
+    float* dst = tile + 4 * Lay::unit(col0) + j;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 4 * h + i;
+        if (o < B) {
+          const int a = LIN ? 4 * (Lay::unit(o * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + o * S) - 4 * Lay::unit(col0);
+          dst[a] = acc[0][h][i];
+          dst[a + PLANE] = acc[1][h][i];
+        }
+      }
+  } else {
+    // rows past a ragged last tile hold the last row's result again (their
+    // inputs re-read the last row), so they store the same bytes over it:
+    // the stores stay unconditional and the wait counts static
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r0 = 4 * q + j;
+      const int r = r0 < nr ? r0 : nr - 1;
+      float v[8] = {acc[q][0].x, acc[q][0].y, acc[q][0].z, acc[q][0].w,
+                    acc[q][1].x, acc[q][1].y, acc[q][1].z, acc[q][1].w};
+      T* y = static_cast<T*>(p.y) + (row0 + r) * p.ldy + col0;
+      if constexpr (std::is_same<T, uint16_t>::value) {
+        st_stream(y, u32x4{pack_bf16x2_hw(v[0], v[1]), pack_bf16x2_hw(v[2], v[3]), pack_bf16x2_hw(v[4], v[5]),
+                           pack_bf16x2_hw(v[6], v[7])});
+      } else {
+        st_stream(y, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+        st_stream(y + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+      }
+    }
+  }
+}
+
+template <class Sch, int N, bool TR, bool DOUT, typename T, typename TB>
+__device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, float (&cf)[4][2][8],
+                                           float (&xv)[2][2][8], int gb, int rot, int j, int64_t row0, int nr) {
+  constexpr int M = Sch::M;
+  constexpr int RT = rounds_before_rt<Sch>(M);
+  constexpr int t = stage_of<Sch, N>();
+  constexpr int r = N - rounds_before_rt<Sch>(t);
+  using Sg = typename At<t, typename Sch::L>::type;
+  constexpr int B = Sg::B, S = Sg::S, R = Sch::D / B / kGPR;
+  constexpr bool DIRECT = DOUT && t == M - 1;
+  constexpr int NP = (N + 3) % RT;
+  constexpr int tp = stage_of<Sch, NP>();
+  constexpr int rp = NP - rounds_before_rt<Sch>(tp);
+  using Sp = typename At<tp, typename Sch::L>::type;
+  constexpr int Rp = Sch::D / Sp::B / kGPR;
+  load_coef<Sp::B, TB, TR>(p, p.st[tp], ((rp + rot) % Rp) * kGPR + gb, j, cf[(N + 3) % 4]);
+  if constexpr (r + 1 < R) read_inputs<Sch, B, S>(tile, ((r + 1 + rot) % R) * kGPR + gb, j, xv[(N + 1) % 2]);
+  products_write<Sch, B, S, DIRECT, T>(p, tile, ((r + rot) % R) * kGPR + gb, cf[N % 4], xv[N % 2], row0, nr, j);
+  if constexpr (r + 1 == R) {
+    __syncthreads();
+    if constexpr (t + 1 < M) {
+      using Sn = typename At<t + 1, typename Sch::L>::type;
+      constexpr int Rn = Sch::D / Sn::B / kGPR;
+      read_inputs<Sch, Sn::B, Sn::S>(tile, (rot % Rn) * kGPR + gb, j, xv[(N + 1) % 2]);
+    }
+  }
+  if constexpr (N + 1 < RT) pipe_round<Sch, N + 1, TR, DOUT, T, TB>(p, tile, cf, xv, gb, rot, j, row0, nr);
+}
+
+template <class Sch, bool TR, bool DOUT, typename T, typename TB>
+__global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
+  constexpr int RT = rounds_before_rt<Sch>(Sch::M);
+  static_assert(RT % 4 == 0, "the coefficient buffers rotate with period 4");
+  extern __shared__ float tile[];
+  int64_t tix = blockIdx.x;
+  if (tix >= p.ntiles) return;   // uniform per workgroup
+  if (threadIdx.x >= 64 * kPCW) {
+    data_waves<T, 64 * kPIOW, 2, typename Sch::Lay>(p, tile, threadIdx.x - 64 * kPCW);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int gb = wave * 16 + (lane >> 2);
+  const int j = lane & 3;
+  // Rounds inside a stage are independent, so each workgroup starts the
+  // round sequence at its own offset: at any moment the CUs of an XCD (which
+  // receives every eighth workgroup) then fetch different parts of the
+  // coefficient array instead of all hitting the same L2 lines.
+  const int rot = (int)((blockIdx.x >> 3) & 0xffff);
+  using S0 = typename At<0, typename Sch::L>::type;
+  constexpr int R0 = Sch::D / S0::B / kGPR;
+  float cf[4][2][8];
+  float xv[2][2][8];
+#pragma unroll
+  for (int n = 0; n < 3; ++n) {
+    // rounds 0..2 all lie in stage 0 (it has at least 4 rounds)
+    load_coef<S0::B, TB, TR>(p, p.st[0], ((n + rot) % R0) * kGPR + gb, j, cf[n]);
+  }
+  __syncthreads();
+  for (; tix < p.ntiles; tix += gridDim.x) {
+    const int64_t row0 = tix * kRows;
+    const int nr = tile_rows(p, tix);
+    read_inputs<Sch, S0::B, S0::S>(tile, (rot % R0) * kGPR + gb, j, xv[0]);
+    pipe_round<Sch, 0, TR, DOUT, T, TB>(p, tile, cf, xv, gb, rot, j, row0, nr);
+    if (!DOUT) __syncthreads();   // data waves copy the tile out
+    __syncthreads();              // data waves write the next tile in
+  }
+}
+
+// Compile-time schedules (processing order; the inverse runs the stages in
+// reverse).  d = 4096 uses the padded layout (147 KiB of LDS); d = 5120 fills
+// the 160 KiB LDS exactly and keeps the unpadded XOR layout.
+using F4096 = Sched<4096, LayPad8, List<St<8, 512>, St<8, 64>, St<8, 8>, St<8, 1>>>;
+using I4096 = Sched<4096, LayPad8, List<St<8, 1>, St<8, 8>, St<8, 64>, St<8, 512>>>;
+using F5120 = Sched<5120, LayXor, List<St<8, 640>, St<8, 80>, St<8, 10>, St<5, 2>, St<2, 1>>>;
+using I5120 = Sched<5120, LayXor, List<St<2, 1>, St<5, 2>, St<8, 10>, St<8, 80>, St<8, 640>>>;
+
+static_assert(linear_stage<LayPad8, 4096, 8, 512>() && linear_stage<LayPad8, 4096, 8, 64>() &&
+                  linear_stage<LayPad8, 4096, 8, 8>() && linear_stage<LayPad8, 4096, 8, 1>(),
+              "padded layout must give constant column offsets for d = 4096, (8,8,8,8)");
+
+template <class Sch, bool TR, bool DOUT, typename T, typename TB>
+hipError_t launch_sched(const RowParams& p, int grid, hipStream_t st) {
+  constexpr bool PIPE = rounds_before_rt<Sch>(Sch::M) % 4 == 0;
+  void (*kern)(RowParams);
+  if constexpr (PIPE) kern = apply_pipe_kernel<Sch, TR, DOUT, T, TB>;
+  else kern = apply_fast_kernel<Sch, TR, DOUT, T, TB>;
+  const size_t lds = (size_t)kRows * 4 * Sch::Lay::units(Sch::D);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(PIPE ? kPThreads : kThreads), lds, st, p);
+  return hipGetLastError();
+}
+
+template <class F, class I, typename T, typename TB>
+hipError_t launch_pair(const RowParams& p, int grid, hipStream_t st) {
+  using Last = typename At<F::M - 1, typename F::L>::type;
+  if (p.transpose) return launch_sched<I, true, false, T, TB>(p, grid, st);
+  if constexpr (Last::B == 8 && Last::S == 1) {
+    if (p.direct_out) return launch_sched<F, false, true, T, TB>(p, grid, st);
+  }
+  return launch_sched<F, false, false, T, TB>(p, grid, st);
+}
+
+template <typename T, typename TB>
+hipError_t launch_d(int d, const RowParams& p, int grid, hipStream_t st) {
+  return d == 4096 ? launch_pair<F4096, I4096, T, TB>(p, grid, st) : launch_pair<F5120, I5120, T, TB>(p, grid, st);
+}
+
+}  // namespace
+
+bool fast_path_supported(const Plan& pl, DT bdt) {
+  if (bdt != DT::F32 && bdt != DT::BF16) return false;
+  static const int r4096[] = {8, 8, 8, 8};
+  static const int r5120[] = {8, 8, 8, 5, 2};
+  const int* want = pl.d == 4096 ? r4096 : (pl.d == 5120 ? r5120 : nullptr);
+  const int m = pl.d == 4096 ? 4 : 5;
+  if (want == nullptr || pl.m != m) return false;
+  for (int t = 0; t < m; ++t)
+    if (pl.radix[t] != want[t]) return false;
+  return true;
+}
+
+hipError_t launch_apply_fast(const Plan& pl, bool inverse, const void* blocks, DT bdt, const int8_t* signs,
+                             const void* x, int64_t ldx, DT io, void* y, int64_t ldy, int64_t rows,
+                             hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  RowParams p = make_row_params(pl, inverse, blocks, nullptr, signs, x, ldx, io, y, ldy, rows);
+  int64_t grid = cu_count();
+  if (grid > p.ntiles) grid = p.ntiles;
+  const int d = (int)pl.d;
+  if (io == DT::BF16)
+    return bdt == DT::F32 ? launch_d<uint16_t, float>(d, p, (int)grid, stream)
+                          : launch_d<uint16_t, uint16_t>(d, p, (int)grid, stream);
+  return bdt == DT::F32 ? launch_d<float, float>(d, p, (int)grid, stream)
+                        : launch_d<float, uint16_t>(d, p, (int)grid, stream);
+}
+
+}  // namespace harp

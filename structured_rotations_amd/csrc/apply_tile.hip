@@ -189,14 +189,17 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
                              int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
                              int64_t rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  // Row-tile kernels: the matrix-core kernel for fp32 and bf16 blocks, the
-  // vector-ALU kernel for int8 blocks (whose coefficient traffic is small
-  // enough that the plain FMA path wins).  HARP_ROW_KERNEL overrides the
-  // choice (1 matrix-core, 2 vector-ALU, 3 generic tile kernel);
-  // HARP_ROW_ROLES picks the wave split.
+  // Row-tile kernels: the schedule-specialised matrix-core kernel where the
+  // schedule has one, else the matrix-core kernel for fp32 and bf16 blocks
+  // and the vector-ALU kernel for int8 blocks (whose coefficient traffic is
+  // small enough that the plain FMA path wins).  HARP_ROW_KERNEL overrides
+  // the choice (1 matrix-core, 2 vector-ALU, 3 generic tile kernel);
+  // HARP_ROW_ROLES picks the matrix-core kernel's wave split.
   static const int row_kernel = env_int("HARP_ROW_KERNEL", 0);
   if (in_dt == out_dt && row_kernel != 3 && row_path_supported(pl, in_dt, blocks, signs, x, ldx, y, ldy)) {
     static const int roles = env_int("HARP_ROW_ROLES", 0);
+    if ((row_kernel == 0 || row_kernel == 4) && fast_path_supported(pl, bdt))
+      return launch_apply_fast(pl, inverse, blocks, bdt, signs, x, ldx, in_dt, y, ldy, rows, stream);
     const bool valu = row_kernel == 2 || (row_kernel == 0 && bdt == DT::I8);
     if (valu)
       return launch_apply_valu(pl, inverse, blocks, bdt, scales, signs, x, ldx, in_dt, y, ldy, rows, roles, stream);

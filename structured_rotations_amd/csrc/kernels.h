@@ -30,6 +30,12 @@ bool row_path_supported(const Plan& pl, DT io, const void* blocks, const int8_t*
 hipError_t launch_apply_valu(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
                              const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
                              int64_t rows, int roles, hipStream_t stream);
+// Schedule-specialised matrix-core kernel: d = 4096 (8,8,8,8) and d = 5120
+// (8,8,8,5,2) with fp32 or bf16 blocks (plus the row-path alignment rules).
+bool fast_path_supported(const Plan& pl, DT bdt);
+hipError_t launch_apply_fast(const Plan& pl, bool inverse, const void* blocks, DT bdt, const int8_t* signs,
+                             const void* x, int64_t ldx, DT io, void* y, int64_t ldy, int64_t rows,
+                             hipStream_t stream);
 hipError_t launch_apply_mfma(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
                              const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
                              int64_t rows, int roles, hipStream_t stream);

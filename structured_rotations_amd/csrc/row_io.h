@@ -51,6 +51,17 @@ __device__ __forceinline__ int fdiv(int n, uint64_t magic) { return (int)(((uint
 // hit every bank once.
 __device__ __forceinline__ int pcol(int c) { return c ^ ((c >> 3) & 15); }
 
+// Unit layouts of a row-quad plane: unit(c) is the 16-byte unit of column c,
+// units(d) the plane size in units.
+struct LayXor {   // the swizzle above, no padding (fits 8 rows of d = 5120)
+  __host__ __device__ static constexpr int unit(int c) { return c ^ ((c >> 3) & 15); }
+  __host__ __device__ static constexpr int units(int d) { return d; }
+};
+struct LayPad8 {  // one padding unit after every 8 columns
+  __host__ __device__ static constexpr int unit(int c) { return c + (c >> 3); }
+  __host__ __device__ static constexpr int units(int d) { return d + d / 8; }
+};
+
 template <typename T> struct Io;
 template <> struct Io<uint16_t> { static constexpr int V = 8; };
 template <> struct Io<float> { static constexpr int V = 4; };
@@ -120,26 +131,25 @@ __device__ __forceinline__ f32x4 io_column(const IoBlock& blk, int u) {
 // Writes a micro-block (rows 4q..4q+3 of the V columns of chunk c).  The
 // chunk's columns c*V + u share bits 3..6 (V <= 8 and chunks are aligned), so
 // their units are (c*V ^ m) ^ u with one mask m.
-template <typename T>
+template <typename T, class Lay = LayXor>
 __device__ __forceinline__ void io_to_lds(const RowParams& p, float* tile, int q, int c, const IoBlock& blk) {
   constexpr int V = Io<T>::V;
-  float* plane = tile + q * 4 * p.d;
-  const int base = pcol(c * V);
+  float* plane = tile + q * 4 * Lay::units(p.d);
 #pragma unroll
   for (int u = 0; u < V; ++u)
-    *reinterpret_cast<f32x4*>(plane + 4 * (base ^ u)) = io_column<T>(blk, u);
+    *reinterpret_cast<f32x4*>(plane + 4 * Lay::unit(c * V + u)) = io_column<T>(blk, u);
 }
 
-template <typename T>
+template <typename T, class Lay = LayXor>
 __device__ __forceinline__ void io_store(const RowParams& p, const float* tile, int64_t row0, int nr, int q, int c) {
   constexpr int V = Io<T>::V;
   T* y = static_cast<T*>(p.y);
-  const float* plane = tile + q * 4 * p.d;
+  const float* plane = tile + q * 4 * Lay::units(p.d);
   float v[4][V];
 #pragma unroll
   for (int u = 0; u < V; ++u) {
     const int col = c * V + u;
-    f32x4 t = *reinterpret_cast<const f32x4*>(plane + 4 * pcol(col));
+    f32x4 t = *reinterpret_cast<const f32x4*>(plane + 4 * Lay::unit(col));
     if (p.sign_mode == 2 && p.signs[col] < 0) {
       t.x = -t.x; t.y = -t.y; t.z = -t.z; t.w = -t.w;
     }
@@ -164,7 +174,7 @@ __device__ __forceinline__ int tile_rows(const RowParams& p, int64_t tix) {
 // to HBM), and write the prefetched tile into LDS.  Barriers per tile:
 // m + (direct_out ? 0 : 1) + 1, after one initial barrier; the compute waves
 // pass the same sequence.
-template <typename T, int kIoThreads, int kMaxIo>
+template <typename T, int kIoThreads, int kMaxIo, class Lay = LayXor>
 __device__ __forceinline__ void data_waves(const RowParams& p, float* tile, int it) {
   int64_t tix = blockIdx.x;
   IoBlock pf[2][kMaxIo];
@@ -174,7 +184,7 @@ __device__ __forceinline__ void data_waves(const RowParams& p, float* tile, int 
       for (int c = it; c < p.chunks; c += kIoThreads) {
         IoBlock one;
         io_load<T>(p, tix * kRows, nr, q, c, one);
-        io_to_lds<T>(p, tile, q, c, one);
+        io_to_lds<T, Lay>(p, tile, q, c, one);
       }
   }
   __syncthreads();
@@ -196,7 +206,7 @@ __device__ __forceinline__ void data_waves(const RowParams& p, float* tile, int 
     for (int t = 0; t < p.m; ++t) __syncthreads();
     if (!p.direct_out) {
       for (int q = 0; q < 2; ++q)
-        for (int c = it; c < p.chunks; c += kIoThreads) io_store<T>(p, tile, row0, nr, q, c);
+        for (int c = it; c < p.chunks; c += kIoThreads) io_store<T, Lay>(p, tile, row0, nr, q, c);
       __syncthreads();
     }
     if (has_next) {
@@ -205,13 +215,13 @@ __device__ __forceinline__ void data_waves(const RowParams& p, float* tile, int 
 #pragma unroll
         for (int u = 0; u < kMaxIo; ++u) {
           const int c = it + u * kIoThreads;
-          if (c < p.chunks) io_to_lds<T>(p, tile, q, c, pf[q][u]);
+          if (c < p.chunks) io_to_lds<T, Lay>(p, tile, q, c, pf[q][u]);
         }
       for (int q = 0; q < 2; ++q)
         for (int c = it + kMaxIo * kIoThreads; c < p.chunks; c += kIoThreads) {
           IoBlock one;
           io_load<T>(p, nxt * kRows, nr_next, q, c, one);
-          io_to_lds<T>(p, tile, q, c, one);
+          io_to_lds<T, Lay>(p, tile, q, c, one);
         }
     }
     __syncthreads();
