@@ -103,37 +103,57 @@ constexpr int rounds_before_rt(int t) {
   }
 }
 
-// cf[h][k] = C[4h + j][k] of group g (C = B forward, B^T inverse); lanes whose
-// row 4h + j is past the radix re-read row B - 1 (their outputs are dropped).
+// Coefficients are read through a buffer resource: the part of the byte
+// offset that is the same for the whole wave (stage, round) goes in an SGPR,
+// the lane's part (its group within the round and its coefficient row) is
+// one 32-bit VGPR that never changes, so a round costs no 64-bit address
+// arithmetic and keeps no per-round pointers live.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coef_rsrc(const RowParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.blocks), (short)0, -1, 0x00020000);
+}
+
+// cf[h][k] = C[4h + j][k] of group g0 + gb (C = B forward, B^T inverse; g0
+// uniform); lanes whose row 4h + j is past the radix re-read row B - 1 (their
+// outputs are dropped).
 template <int B, typename TB, bool TR>
-__device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g, int j, float (&cf)[2][8]) {
-  const TB* blk = static_cast<const TB*>(p.blocks) + sd.blk_off + (int64_t)g * B * B;
+__device__ __forceinline__ void load_coef(__amdgpu_buffer_rsrc_t rs, const StageFast& sd, int g0, int gb, int j,
+                                          float (&cf)[2][8]) {
   constexpr int NH = B > 4 ? 2 : 1;
+  constexpr int SZ = (int)sizeof(TB);
+  const int soff = __builtin_amdgcn_readfirstlane((sd.blk_off + g0 * B * B) * SZ);
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int o = 4 * h + j < B ? 4 * h + j : B - 1;
     if constexpr (!TR && (B == 8 || B == 4)) {
-      const TB* row = blk + o * B;
+      const int voff = (gb * B * B + o * B) * SZ;
       if constexpr (std::is_same<TB, float>::value) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(row);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
         cf[h][0] = __uint_as_float(a.x); cf[h][1] = __uint_as_float(a.y);
         cf[h][2] = __uint_as_float(a.z); cf[h][3] = __uint_as_float(a.w);
         if constexpr (B == 8) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(row + 4);
+          const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, 0);
           cf[h][4] = __uint_as_float(b.x); cf[h][5] = __uint_as_float(b.y);
           cf[h][6] = __uint_as_float(b.z); cf[h][7] = __uint_as_float(b.w);
         }
       } else if constexpr (B == 8) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(row);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
         cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
         cf[h][4] = bf16_lo(a.z); cf[h][5] = bf16_hi(a.z); cf[h][6] = bf16_lo(a.w); cf[h][7] = bf16_hi(a.w);
       } else {
-        const uint2 a = *reinterpret_cast<const uint2*>(row);
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
         cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
       }
     } else {
+      // element (o, k) of C sits at k * B + o (transposed) or o * B + k
+      const int voff = (gb * B * B + (TR ? o : o * B)) * SZ;
 #pragma unroll
-      for (int k = 0; k < B; ++k) cf[h][k] = coef<TB>(blk, TR ? k * B + o : o * B + k, 1.0f);
+      for (int k = 0; k < B; ++k) {
+        const int imm = (TR ? k * B : k) * SZ;
+        if constexpr (std::is_same<TB, float>::value)
+          cf[h][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff + imm, soff, 0));
+        else
+          cf[h][k] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff + imm, soff, 0) << 16);
+      }
     }
   }
 }
@@ -225,27 +245,28 @@ __device__ __forceinline__ void run_stage(const RowParams& p, float* tile, float
   float(&Y)[2][8] = SW ? ca : cb;
   const StageFast& sd = p.st[I];
   const StageFast& sn = p.st[(I + 1) % M];
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   if constexpr (R % 2 == 0) {
 #pragma unroll 1
     for (int r = 0; r < R - 2; r += 2) {
-      load_coef<B, TB, TR>(p, sd, (r + 1) * kGPR + gb, j, Y);
+      load_coef<B, TB, TR>(rs, sd, (r + 1) * kGPR, gb, j, Y);
       round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, r * kGPR + gb, X, row0, nr, j);
-      load_coef<B, TB, TR>(p, sd, (r + 2) * kGPR + gb, j, X);
+      load_coef<B, TB, TR>(rs, sd, (r + 2) * kGPR, gb, j, X);
       round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (r + 1) * kGPR + gb, Y, row0, nr, j);
     }
-    load_coef<B, TB, TR>(p, sd, (R - 1) * kGPR + gb, j, Y);
+    load_coef<B, TB, TR>(rs, sd, (R - 1) * kGPR, gb, j, Y);
     round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 2) * kGPR + gb, X, row0, nr, j);
-    load_coef<Sn::B, TB, TR>(p, sn, gb, j, X);
+    load_coef<Sn::B, TB, TR>(rs, sn, 0, gb, j, X);
     round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 1) * kGPR + gb, Y, row0, nr, j);
   } else {
 #pragma unroll 1
     for (int r = 0; r < R - 1; r += 2) {
-      load_coef<B, TB, TR>(p, sd, (r + 1) * kGPR + gb, j, Y);
+      load_coef<B, TB, TR>(rs, sd, (r + 1) * kGPR, gb, j, Y);
       round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, r * kGPR + gb, X, row0, nr, j);
-      load_coef<B, TB, TR>(p, sd, (r + 2) * kGPR + gb, j, X);
+      load_coef<B, TB, TR>(rs, sd, (r + 2) * kGPR, gb, j, X);
       round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (r + 1) * kGPR + gb, Y, row0, nr, j);
     }
-    load_coef<Sn::B, TB, TR>(p, sn, gb, j, Y);
+    load_coef<Sn::B, TB, TR>(rs, sn, 0, gb, j, Y);
     round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 1) * kGPR + gb, X, row0, nr, j);
   }
   __syncthreads();
@@ -281,7 +302,7 @@ __global__ void __launch_bounds__(kThreads) apply_fast_kernel(RowParams p) {
   const int j = lane & 3;
   float ca[2][8], cb[2][8];
   using S0 = typename At<0, typename Sch::L>::type;
-  load_coef<S0::B, TB, TR>(p, p.st[0], gb, j, ca);
+  load_coef<S0::B, TB, TR>(coef_rsrc(p), p.st[0], 0, gb, j, ca);
   __syncthreads();
   while (true) {
     tile_body<Sch, false, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, tix);
@@ -333,40 +354,63 @@ __device__ __forceinline__ void read_inputs(const float* tile, int g, int j, flo
   }
 }
 
-template <class Sch, int B, int S, bool DIRECT, typename T>
-__device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, const float (&cf)[2][8],
-                                               const float (&xv)[2][8], int64_t row0, int nr, int j) {
+// One round of products, ordered so that no LDS latency lands on the matrix
+// cores: the h = 0 outputs are written while the h = 1 chain runs, the next
+// round's inputs are read after those writes (so the next round waits only
+// for its own reads and the writes before them, never for the last writes),
+// and the h = 1 outputs go last.  Radix 8 only (two output halves).
+template <class Sch, int B, int S, bool DIRECT, bool NEXT, typename T>
+__device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, int gn, const float (&cf)[2][8],
+                                               const float (&xv)[2][8], float (&xn)[2][8], int64_t row0, int nr,
+                                               int j) {
+  static_assert(B == 8, "the pipelined round is written for radix 8");
   using Lay = typename Sch::Lay;
-  constexpr int NH = B > 4 ? 2 : 1;
   constexpr int PLANE = 4 * Lay::units(Sch::D);
   constexpr bool LIN = linear_stage<Lay, Sch::D, B, S>();
   const int col0 = col0_of<B, S>(g);
+  float* dst = tile + 4 * Lay::unit(col0) + j;
+  auto out_addr = [&](int o) {
+    return LIN ? 4 * (Lay::unit(o * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + o * S) - 4 * Lay::unit(col0);
+  };
   f32x4 acc[2][2];
 #pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  for (int q = 0; q < 2; ++q)
+    acc[q][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[0][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
   for (int k = 1; k < B; ++k)
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int q = 0; q < 2; ++q)
+      acc[q][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[0][k], xv[q][k], acc[q][0], 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        acc[q][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][k], xv[q][k], acc[q][h], 0, 0, 0);
+  for (int q = 0; q < 2; ++q)
+    acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[1][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[1][1], xv[q][1], acc[q][1], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (!DIRECT) {
-    float* dst = tile + 4 * Lay::unit(col0) + j;
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int i = 0; i < 4; ++i) {
+      dst[out_addr(i)] = acc[0][0][i];
+      dst[out_addr(i) + PLANE] = acc[1][0][i];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NEXT) read_inputs<Sch, B, S>(tile, gn, j, xn);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = 4 * h + i;
-        if (o < B) {
-          const int a = LIN ? 4 * (Lay::unit(o * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + o * S) - 4 * Lay::unit(col0);
-          dst[a] = acc[0][h][i];
-          dst[a + PLANE] = acc[1][h][i];
-        }
-      }
+  for (int k = 2; k < B; ++k) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[1][k], xv[q][k], acc[q][1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!DIRECT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dst[out_addr(4 + i)] = acc[0][1][i];
+      dst[out_addr(4 + i) + PLANE] = acc[1][1][i];
+    }
   } else {
     // rows past a ragged last tile hold the last row's result again (their
     // inputs re-read the last row), so they store the same bytes over it:
@@ -389,9 +433,32 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
   }
 }
 
+// Wave-local group sets.  For d = 4096 = 64 x 64 (column c = 64 hi + lo), in
+// the two stages on the digits of hi (strides 512 and 64) wave w takes the
+// groups whose lo lies in [8w, 8w + 8), and in the two stages on the digits
+// of lo (strides 8 and 1) those whose hi lies in [8w, 8w + 8).  Inside each
+// pair of stages a wave therefore reads only columns it wrote itself, so the
+// pair needs no workgroup barrier in between (LDS accesses of one wave are
+// performed in order); only the change of pair is an all-to-all exchange.
+// Round rr of a stage covers, per wave, 16 groups: the uniform part of the
+// group index is grp_round(rr), the lane's part lane_grp(gA, gB).
+template <int S>
+constexpr bool hi_pair() {
+  return S >= 64;
+}
+template <int S>
+__device__ __forceinline__ int grp_round(int rr) {
+  return hi_pair<S>() ? rr * 128 : rr * 16;
+}
+template <int S>
+__device__ __forceinline__ int lane_grp(int gA, int gB) {
+  return hi_pair<S>() ? gA : gB;
+}
+
 template <class Sch, int N, bool TR, bool DOUT, typename T, typename TB>
 __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, float (&cf)[4][2][8],
-                                           float (&xv)[2][2][8], int gb, int rot, int j, int64_t row0, int nr) {
+                                           float (&xv)[2][2][8], int gA, int gB, int rot, int j, int64_t row0,
+                                           int nr) {
   constexpr int M = Sch::M;
   constexpr int RT = rounds_before_rt<Sch>(M);
   constexpr int t = stage_of<Sch, N>();
@@ -404,34 +471,115 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   constexpr int rp = NP - rounds_before_rt<Sch>(tp);
   using Sp = typename At<tp, typename Sch::L>::type;
   constexpr int Rp = Sch::D / Sp::B / kGPR;
-  load_coef<Sp::B, TB, TR>(p, p.st[tp], ((rp + rot) % Rp) * kGPR + gb, j, cf[(N + 3) % 4]);
-  if constexpr (r + 1 < R) read_inputs<Sch, B, S>(tile, ((r + 1 + rot) % R) * kGPR + gb, j, xv[(N + 1) % 2]);
-  products_write<Sch, B, S, DIRECT, T>(p, tile, ((r + rot) % R) * kGPR + gb, cf[N % 4], xv[N % 2], row0, nr, j);
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
+  const int gl = lane_grp<S>(gA, gB);
+  __builtin_amdgcn_sched_barrier(0);
+  load_coef<Sp::B, TB, TR>(rs, p.st[tp], grp_round<Sp::S>((rp + rot) % Rp), lane_grp<Sp::S>(gA, gB), j,
+                           cf[(N + 3) % 4]);
+  __builtin_amdgcn_sched_barrier(0);
+  products_write<Sch, B, S, DIRECT, (r + 1 < R), T>(p, tile, grp_round<S>((r + rot) % R) + gl,
+                                                   grp_round<S>((r + 1 + rot) % R) + gl, cf[N % 4], xv[N % 2],
+                                                   xv[(N + 1) % 2], row0, nr, j);
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (r + 1 == R) {
-    __syncthreads();
     if constexpr (t + 1 < M) {
       using Sn = typename At<t + 1, typename Sch::L>::type;
       constexpr int Rn = Sch::D / Sn::B / kGPR;
-      read_inputs<Sch, Sn::B, Sn::S>(tile, (rot % Rn) * kGPR + gb, j, xv[(N + 1) % 2]);
+      if constexpr (hi_pair<S>() != hi_pair<Sn::S>()) {
+        __syncthreads();
+      } else {
+        // the next stage reads what this wave has just written
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      read_inputs<Sch, Sn::B, Sn::S>(tile, grp_round<Sn::S>(rot % Rn) + lane_grp<Sn::S>(gA, gB), j,
+                                     xv[(N + 1) % 2]);
+    } else {
+      __syncthreads();   // the tile is finished
     }
   }
-  if constexpr (N + 1 < RT) pipe_round<Sch, N + 1, TR, DOUT, T, TB>(p, tile, cf, xv, gb, rot, j, row0, nr);
+  if constexpr (N + 1 < RT) pipe_round<Sch, N + 1, TR, DOUT, T, TB>(p, tile, cf, xv, gA, gB, rot, j, row0, nr);
+}
+
+// Data waves of the pipelined kernel: per tile they issue the next tile's
+// loads, pass the exchange barrier in the middle of the tile and the barrier
+// after its last stage, copy the finished tile out (unless the last stage was
+// stored straight to HBM), write the prefetched tile in, and release the
+// compute waves with a third barrier.  Each data thread copies out and then
+// overwrites the same chunks, so no barrier is needed between the two.
+template <typename T, class Lay, bool DOUT>
+__device__ __forceinline__ void pipe_data_waves(const RowParams& p, float* tile, int it) {
+  constexpr int kIoT = 64 * kPIOW;
+  constexpr int kMaxIo = 2;
+  int64_t tix = blockIdx.x;
+  IoBlock pf[2][kMaxIo];
+  {
+    const int nr = tile_rows(p, tix);
+    for (int q = 0; q < 2; ++q)
+      for (int c = it; c < p.chunks; c += kIoT) {
+        IoBlock one;
+        io_load<T>(p, tix * kRows, nr, q, c, one);
+        io_to_lds<T, Lay>(p, tile, q, c, one);
+      }
+  }
+  __syncthreads();
+  for (; tix < p.ntiles; tix += gridDim.x) {
+    const int64_t row0 = tix * kRows;
+    const int nr = tile_rows(p, tix);
+    const int64_t nxt = tix + gridDim.x;
+    const bool has_next = nxt < p.ntiles;
+    const int nr_next = has_next ? tile_rows(p, nxt) : 0;
+    if (has_next) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int u = 0; u < kMaxIo; ++u) {
+          const int c = it + u * kIoT;
+          if (c < p.chunks) io_load<T>(p, nxt * kRows, nr_next, q, c, pf[q][u]);
+        }
+    }
+    __syncthreads();   // exchange between the two pairs of stages
+    __syncthreads();   // last stage done
+    if constexpr (!DOUT) {
+      for (int q = 0; q < 2; ++q)
+        for (int c = it; c < p.chunks; c += kIoT) io_store<T, Lay>(p, tile, row0, nr, q, c);
+    }
+    if (has_next) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int u = 0; u < kMaxIo; ++u) {
+          const int c = it + u * kIoT;
+          if (c < p.chunks) io_to_lds<T, Lay>(p, tile, q, c, pf[q][u]);
+        }
+      for (int q = 0; q < 2; ++q)
+        for (int c = it + kMaxIo * kIoT; c < p.chunks; c += kIoT) {
+          IoBlock one;
+          io_load<T>(p, nxt * kRows, nr_next, q, c, one);
+          io_to_lds<T, Lay>(p, tile, q, c, one);
+        }
+    }
+    __syncthreads();   // next tile in place
+  }
 }
 
 template <class Sch, bool TR, bool DOUT, typename T, typename TB>
 __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
   constexpr int RT = rounds_before_rt<Sch>(Sch::M);
   static_assert(RT % 4 == 0, "the coefficient buffers rotate with period 4");
+  static_assert(Sch::D == 4096 && kGPR == 128, "wave-local group sets are laid out for d = 4096");
   extern __shared__ float tile[];
   int64_t tix = blockIdx.x;
   if (tix >= p.ntiles) return;   // uniform per workgroup
   if (threadIdx.x >= 64 * kPCW) {
-    data_waves<T, 64 * kPIOW, 2, typename Sch::Lay>(p, tile, threadIdx.x - 64 * kPCW);
+    pipe_data_waves<T, typename Sch::Lay, DOUT>(p, tile, threadIdx.x - 64 * kPCW);
     return;
   }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int gb = wave * 16 + (lane >> 2);
+  const int blk = lane >> 2;
+  const int gA = (blk >> 3) * 64 + 8 * wave + (blk & 7);
+  const int gB = 64 * wave + blk;
   const int j = lane & 3;
   // Rounds inside a stage are independent, so each workgroup starts the
   // round sequence at its own offset: at any moment the CUs of an XCD (which
@@ -445,16 +593,16 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
 #pragma unroll
   for (int n = 0; n < 3; ++n) {
     // rounds 0..2 all lie in stage 0 (it has at least 4 rounds)
-    load_coef<S0::B, TB, TR>(p, p.st[0], ((n + rot) % R0) * kGPR + gb, j, cf[n]);
+    load_coef<S0::B, TB, TR>(coef_rsrc(p), p.st[0], grp_round<S0::S>((n + rot) % R0), lane_grp<S0::S>(gA, gB), j,
+                             cf[n]);
   }
   __syncthreads();
   for (; tix < p.ntiles; tix += gridDim.x) {
     const int64_t row0 = tix * kRows;
     const int nr = tile_rows(p, tix);
-    read_inputs<Sch, S0::B, S0::S>(tile, (rot % R0) * kGPR + gb, j, xv[0]);
-    pipe_round<Sch, 0, TR, DOUT, T, TB>(p, tile, cf, xv, gb, rot, j, row0, nr);
-    if (!DOUT) __syncthreads();   // data waves copy the tile out
-    __syncthreads();              // data waves write the next tile in
+    read_inputs<Sch, S0::B, S0::S>(tile, grp_round<S0::S>(rot % R0) + lane_grp<S0::S>(gA, gB), j, xv[0]);
+    pipe_round<Sch, 0, TR, DOUT, T, TB>(p, tile, cf, xv, gA, gB, rot, j, row0, nr);
+    __syncthreads();   // data waves have copied the tile out and written the next one in
   }
 }
 

@@ -262,6 +262,8 @@ __device__ __forceinline__ void transpose(float (&v)[1 << Lay<N>::EB], float* bu
       if (S < 0 || ((r >> 2) & 1) == h) {   // register bit 2 holds e bit SPLIT in both layouts
         f32x4 w = {v[r], v[r + 1], v[r + 2], v[r + 3]};
         *reinterpret_cast<f32x4*>(buf + (lw ^ buf_off<N>(reg_part<N, FROM>(r)))) = w;
+        // a few accesses at a time: hoisting all addresses costs registers
+        if ((r & 31) == 28) __builtin_amdgcn_sched_barrier(0);
       }
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -270,6 +272,7 @@ __device__ __forceinline__ void transpose(float (&v)[1 << Lay<N>::EB], float* bu
       if (S < 0 || ((r >> 2) & 1) == h) {
         const f32x4 w = *reinterpret_cast<const f32x4*>(buf + (lr ^ buf_off<N>(reg_part<N, TO>(r))));
         v[r] = w.x; v[r + 1] = w.y; v[r + 2] = w.z; v[r + 3] = w.w;
+        if ((r & 31) == 28) __builtin_amdgcn_sched_barrier(0);
       }
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -302,8 +305,12 @@ template <typename T> struct IoV;
 template <> struct IoV<uint16_t> { static constexpr int V = 8; };
 template <> struct IoV<float> { static constexpr int V = 4; };
 
-template <int N, typename T, bool INV>
-__global__ void __launch_bounds__(512) rht_wave_kernel(WaveParams p) {
+// WPB waves per workgroup (8: two waves per SIMD).  For d = 8192 (128
+// coordinates per lane) the 256-register budget spills a few dozen values;
+// one wave per SIMD avoids the spills but measured slower (the second wave
+// hides the LDS and memory latencies).
+template <int N, typename T, bool INV, int WPB>
+__global__ void __launch_bounds__(64 * WPB) rht_wave_kernel(WaveParams p) {
   constexpr int EB = Lay<N>::EB;
   constexpr int E = 1 << EB;
   constexpr int NW = E / 32;                 // sign words per lane per pass
@@ -429,15 +436,16 @@ hipError_t launch_rht_typed(const TileParams& p, const RhtExtra& ex, int threads
 }
 template <int N, typename T, bool INV>
 hipError_t launch_wave_typed(const rhtw::WaveParams& wp, hipStream_t stream) {
-  auto kern = rhtw::rht_wave_kernel<N, T, INV>;
-  const size_t lds = (size_t)8 * 64 * ((1 << (N - 6)) / 32) * 4 + (size_t)8 * 4096 * 4;
+  constexpr int WPB = 8;
+  auto kern = rhtw::rht_wave_kernel<N, T, INV, WPB>;
+  const size_t lds = (size_t)8 * 64 * ((1 << (N - 6)) / 32) * 4 + (size_t)WPB * 4096 * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   int64_t grid = cu_count();
-  const int64_t need = (wp.rows + 7) / 8;
+  const int64_t need = (wp.rows + WPB - 1) / WPB;
   if (grid > need) grid = need;
-  hipLaunchKernelGGL(kern, dim3((int)grid), dim3(512), lds, stream, wp);
+  hipLaunchKernelGGL(kern, dim3((int)grid), dim3(64 * WPB), lds, stream, wp);
   return hipGetLastError();
 }
 

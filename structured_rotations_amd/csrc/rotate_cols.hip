@@ -52,11 +52,18 @@ __device__ __forceinline__ float ld_el(const uint16_t* p) { return bf16_to_f32(*
 __device__ __forceinline__ void st_el(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st_el(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_rne(v); }
 
+// Row stride of a staged block in LDS: each output row of C starts on a
+// 16-byte boundary so a task reads it with 128-bit broadcast loads.
+template <int B>
+constexpr int coef_row_stride() { return (B + 3) & ~3; }
+
 // Stage the coefficients of the tile's groups for one stage into LDS as
-// fp32 C[o][k] (C = B forward, B^T inverse; int8 blocks dequantised), so the
-// stage's tasks read them with broadcast LDS loads.
+// fp32 C[o][k] (C = B forward, B^T inverse; int8 blocks dequantised), rows
+// padded to coef_row_stride<B>() floats, so the stage's tasks read them with
+// broadcast LDS loads.
 template <int B, typename TB>
 __device__ void stage_coefs(const ColParams& p, const ColStage& cs, float* cbuf, int64_t pre, int64_t q) {
+  constexpr int Bp = coef_row_stride<B>();
   const int ngl = p.nsub / B;
   const TB* blocks = static_cast<const TB*>(p.blocks) + cs.blk_off;
   for (int e = threadIdx.x; e < ngl * B * B; e += blockDim.x) {
@@ -66,16 +73,19 @@ __device__ void stage_coefs(const ColParams& p, const ColStage& cs, float* cbuf,
     const int64_t c = pre * (int64_t)ngl * p.suf + (int64_t)gl * p.suf + q;
     float scale = 1.0f;
     if constexpr (std::is_same<TB, int8_t>::value) scale = p.scales[cs.grp_off + c];
-    cbuf[e] = coef<TB>(blocks, c * B * B + (p.transpose ? k * B + o : i), scale);
+    cbuf[gl * (B * Bp) + o * Bp + k] = coef<TB>(blocks, c * B * B + (p.transpose ? k * B + o : i), scale);
   }
 }
 
 // One stage of the run on the tile.  The tile is [nsub][pw] fp32; a task is
 // one group of the stage and a block of 64 columns, one column per lane, so
-// every lane of a wave uses the same coefficients (read from cbuf).
+// every lane of a wave uses the same coefficients (read from cbuf).  All
+// reads of a task come before its stores (the tile and the coefficients
+// never overlap), so they are issued back to back.
 template <int B>
-__device__ void col_stage(const ColParams& p, const ColStage& cs, float* tile, const float* cbuf, int wave,
-                          int nwaves, int lane) {
+__device__ void col_stage(const ColParams& p, const ColStage& cs, float* __restrict__ tile,
+                          const float* __restrict__ cbuf, int wave, int nwaves, int lane) {
+  constexpr int Bp = coef_row_stride<B>();
   const int ngl = p.nsub / B;             // local groups in the tile
   const int ncb = p.pw / 64;              // 64-column blocks
   const int ntask = ngl * ncb;
@@ -86,18 +96,24 @@ __device__ void col_stage(const ColParams& p, const ColStage& cs, float* tile, c
     const int u_lo = gl % ls;
     const int u_hi = gl / ls;
     const int ubase = u_hi * B * ls + u_lo;
-    const float* cf = cbuf + gl * B * B;
+    const f32x4* cf = reinterpret_cast<const f32x4*>(cbuf + gl * (B * Bp));
     float* col = tile + ubase * p.pw + cb * 64 + lane;
     float v[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) v[k] = col[k * ls * p.pw];
+    float acc[B];
 #pragma unroll
     for (int o = 0; o < B; ++o) {
-      float acc = 0.0f;
+      f32x4 c4[Bp / 4];
 #pragma unroll
-      for (int k = 0; k < B; ++k) acc = fmaf(cf[o * B + k], v[k], acc);
-      col[o * ls * p.pw] = acc;
+      for (int j = 0; j < Bp / 4; ++j) c4[j] = cf[o * (Bp / 4) + j];
+      float a = 0.0f;
+#pragma unroll
+      for (int k = 0; k < B; ++k) a = fmaf(c4[k >> 2][k & 3], v[k], a);
+      acc[o] = a;
     }
+#pragma unroll
+    for (int o = 0; o < B; ++o) col[o * ls * p.pw] = acc[o];
   }
 }
 
@@ -291,7 +307,7 @@ __device__ __forceinline__ void col_to_lds(const ColParams& p, const ColTile& t,
 template <typename TIN, typename TOUT, typename TB, bool BIG>
 __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   extern __shared__ float tile[];
-  float* cbuf = tile + p.nsub * p.pw;     // one stage's coefficients (nsub * radix floats)
+  float* cbuf = tile + p.nsub * p.pw;     // one stage's coefficients (nsub * padded row floats)
   constexpr int VI = ColIo<TIN>::V, VO = ColIo<TOUT>::V;
   constexpr int MAXC = VI == 8 ? 8 : 16;
   const TIN* x = static_cast<const TIN*>(p.x);
@@ -439,9 +455,12 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   const int ib = io_bytes(in_dt), ob = io_bytes(out_dt);
   p.vec_in = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (ldx * ib) % 16 == 0;
   p.vec_out = reinterpret_cast<uintptr_t>(y) % 16 == 0 && (ldy * ob) % 16 == 0;
-  int bmax = 2;
-  for (int t = t0; t < t1; ++t) bmax = pl.radix[t] > bmax ? pl.radix[t] : bmax;
-  const size_t lds = ((size_t)nsub * pw + (size_t)nsub * bmax) * sizeof(float);
+  int bmax = 2, cw = 4;   // largest radix; widest padded coefficient row (a stage stages nsub * row floats)
+  for (int t = t0; t < t1; ++t) {
+    bmax = pl.radix[t] > bmax ? pl.radix[t] : bmax;
+    cw = ((pl.radix[t] + 3) & ~3) > cw ? ((pl.radix[t] + 3) & ~3) : cw;
+  }
+  const size_t lds = ((size_t)nsub * pw + (size_t)nsub * cw) * sizeof(float);
   int64_t grid = (int64_t)cus_for_cols() * (lds > 80 * 1024 ? 1 : 2);
   if (grid > p.ntiles) grid = p.ntiles;
   if (in_dt == DT::F32 && out_dt == DT::F32) return launch_cols_blk<float, float>(bdt, p, bmax > 8, (int)grid, lds, stream);
