@@ -501,68 +501,6 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   if constexpr (N + 1 < RT) pipe_round<Sch, N + 1, TR, DOUT, T, TB>(p, tile, cf, xv, gA, gB, rot, j, row0, nr);
 }
 
-// Data waves of the pipelined kernel: per tile they issue the next tile's
-// loads, pass the exchange barrier in the middle of the tile and the barrier
-// after its last stage, copy the finished tile out (unless the last stage was
-// stored straight to HBM), write the prefetched tile in, and release the
-// compute waves with a third barrier.  Each data thread copies out and then
-// overwrites the same chunks, so no barrier is needed between the two.
-template <typename T, class Lay, bool DOUT>
-__device__ __forceinline__ void pipe_data_waves(const RowParams& p, float* tile, int it) {
-  constexpr int kIoT = 64 * kPIOW;
-  constexpr int kMaxIo = 2;
-  int64_t tix = blockIdx.x;
-  IoBlock pf[2][kMaxIo];
-  {
-    const int nr = tile_rows(p, tix);
-    for (int q = 0; q < 2; ++q)
-      for (int c = it; c < p.chunks; c += kIoT) {
-        IoBlock one;
-        io_load<T>(p, tix * kRows, nr, q, c, one);
-        io_to_lds<T, Lay>(p, tile, q, c, one);
-      }
-  }
-  __syncthreads();
-  for (; tix < p.ntiles; tix += gridDim.x) {
-    const int64_t row0 = tix * kRows;
-    const int nr = tile_rows(p, tix);
-    const int64_t nxt = tix + gridDim.x;
-    const bool has_next = nxt < p.ntiles;
-    const int nr_next = has_next ? tile_rows(p, nxt) : 0;
-    if (has_next) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int u = 0; u < kMaxIo; ++u) {
-          const int c = it + u * kIoT;
-          if (c < p.chunks) io_load<T>(p, nxt * kRows, nr_next, q, c, pf[q][u]);
-        }
-    }
-    __syncthreads();   // exchange between the two pairs of stages
-    __syncthreads();   // last stage done
-    if constexpr (!DOUT) {
-      for (int q = 0; q < 2; ++q)
-        for (int c = it; c < p.chunks; c += kIoT) io_store<T, Lay>(p, tile, row0, nr, q, c);
-    }
-    if (has_next) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int u = 0; u < kMaxIo; ++u) {
-          const int c = it + u * kIoT;
-          if (c < p.chunks) io_to_lds<T, Lay>(p, tile, q, c, pf[q][u]);
-        }
-      for (int q = 0; q < 2; ++q)
-        for (int c = it + kMaxIo * kIoT; c < p.chunks; c += kIoT) {
-          IoBlock one;
-          io_load<T>(p, nxt * kRows, nr_next, q, c, one);
-          io_to_lds<T, Lay>(p, tile, q, c, one);
-        }
-    }
-    __syncthreads();   // next tile in place
-  }
-}
-
 template <class Sch, bool TR, bool DOUT, typename T, typename TB>
 __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
   constexpr int RT = rounds_before_rt<Sch>(Sch::M);
@@ -572,7 +510,9 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
   int64_t tix = blockIdx.x;
   if (tix >= p.ntiles) return;   // uniform per workgroup
   if (threadIdx.x >= 64 * kPCW) {
-    pipe_data_waves<T, typename Sch::Lay, DOUT>(p, tile, threadIdx.x - 64 * kPCW);
+    // 2 x 512 (bf16) or 2 x 1024 (fp32) micro-blocks over 256 data threads
+    constexpr bool F = std::is_same<T, float>::value;
+    data_waves_exact<T, typename Sch::Lay, 64 * kPIOW, F ? 8 : 4, 4, 2, DOUT>(p, tile, threadIdx.x - 64 * kPCW);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -602,7 +542,276 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
     const int nr = tile_rows(p, tix);
     read_inputs<Sch, S0::B, S0::S>(tile, grp_round<S0::S>(rot % R0) + lane_grp<S0::S>(gA, gB), j, xv[0]);
     pipe_round<Sch, 0, TR, DOUT, T, TB>(p, tile, cf, xv, gA, gB, rot, j, row0, nr);
-    __syncthreads();   // data waves have copied the tile out and written the next one in
+    __syncthreads();   // data waves have swapped the tile
+  }
+}
+
+// ------------------------------------------------------------------------
+// d = 5120, (8,8,8,5,2).  The radix-5 stage (stride 2) and the radix-2 stage
+// (stride 1) both act inside the 10 consecutive columns 10 hi .. 10 hi + 9
+// of one value hi of the first three digits, so one round does both for 16
+// such chunks per compute wave: the radix-5 products on the matrix cores and
+// the 2 x 2 blocks on the vector ALU, in registers, with one LDS round trip
+// for the pair instead of two and 4 rounds instead of 28.  Operands are
+// swapped against the radix-8 rounds (the data is the A operand): lane j then
+// ends with output 4h + j of the radix-5 block for the four rows of its quad,
+// so both halves d4 = 0, 1 of a radix-2 pair sit in the same lane, and each
+// result is one 16-byte unit (4 rows of one column) of the tile.
+// Coefficient buffer of a round: radix-8 rounds use the first 16 floats as
+// cf[h][k]; tail rounds use [0, 20) for the radix-5 operands c5[d4][h][k]
+// and [20, 40) for 2 x 2 blocks.
+struct Cbuf {
+  float v[40];
+};
+__device__ __forceinline__ float (&as8(Cbuf& c))[2][8] { return *reinterpret_cast<float(*)[2][8]>(&c.v[0]); }
+__device__ __forceinline__ const float (&as8(const Cbuf& c))[2][8] {
+  return *reinterpret_cast<const float(*)[2][8]>(&c.v[0]);
+}
+
+template <typename TB>
+__device__ __forceinline__ float ld_coef1(__amdgpu_buffer_rsrc_t rs, int voff_el, int soff_bytes) {
+  if constexpr (std::is_same<TB, float>::value)
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff_el * 4, soff_bytes, 0));
+  else
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff_el * 2, soff_bytes, 0) << 16);
+}
+// four consecutive coefficients starting at a 4-aligned element
+template <typename TB>
+__device__ __forceinline__ void ld_coef4(__amdgpu_buffer_rsrc_t rs, int voff_el, int soff_bytes, float* d) {
+  if constexpr (std::is_same<TB, float>::value) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_el * 4, soff_bytes, 0);
+    d[0] = __uint_as_float(a.x); d[1] = __uint_as_float(a.y); d[2] = __uint_as_float(a.z); d[3] = __uint_as_float(a.w);
+  } else {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_el * 2, soff_bytes, 0);
+    d[0] = bf16_lo(a.x); d[1] = bf16_hi(a.x); d[2] = bf16_lo(a.y); d[3] = bf16_hi(a.y);
+  }
+}
+
+// Tail coefficients for chunk g = g0 + gb (g0 uniform).  s5: the radix-5
+// stage, s2: the radix-2 stage.  Forward: c5[d4][h][k] = C5_{2g+d4}[o][k],
+// o = min(4h + j, 4), and the two 2 x 2 blocks of columns o (h = 0, 1).
+// Inverse: c5[d4][h][k] = C5_{2g+d4}[k][o] and all five 2 x 2 blocks.
+template <typename TB, bool TR>
+__device__ __forceinline__ void load_tail(__amdgpu_buffer_rsrc_t rs, const StageFast& s5, const StageFast& s2, int g0,
+                                          int gb, int j, Cbuf& c) {
+  constexpr int SZ = (int)sizeof(TB);
+  const int soff5 = __builtin_amdgcn_readfirstlane((s5.blk_off + g0 * 2 * 25) * SZ);
+  const int soff2 = __builtin_amdgcn_readfirstlane((s2.blk_off + g0 * 5 * 4) * SZ);
+#pragma unroll
+  for (int d4 = 0; d4 < 2; ++d4)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = 4 * h + j < 5 ? 4 * h + j : 4;
+      const int base = (2 * gb + d4) * 25;
+      float* d = &c.v[(d4 * 2 + h) * 5];
+      if constexpr (!TR && std::is_same<TB, float>::value) {
+        // row o of the block: 5 consecutive floats, 4-byte aligned (a
+        // 16-byte load needs only dword alignment here)
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + o * 5) * 4, soff5, 0);
+        d[0] = __uint_as_float(a.x); d[1] = __uint_as_float(a.y); d[2] = __uint_as_float(a.z); d[3] = __uint_as_float(a.w);
+        d[4] = ld_coef1<TB>(rs, base + o * 5 + 4, soff5);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 5; ++k) d[k] = ld_coef1<TB>(rs, base + (TR ? k * 5 + o : o * 5 + k), soff5);
+      }
+    }
+  if constexpr (!TR) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = 4 * h + j < 5 ? 4 * h + j : 4;
+      ld_coef4<TB>(rs, (5 * gb + o) * 4, soff2, &c.v[20 + 4 * h]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) ld_coef4<TB>(rs, (5 * gb + k) * 4, soff2, &c.v[20 + 4 * k]);
+  }
+}
+
+template <class Lay, bool TR>
+__device__ __forceinline__ void tail_round(float* tile, int g, const Cbuf& c, int j) {
+  constexpr int PLANE = 4 * Lay::units(5120);
+  const int col0 = 10 * g;
+  float x[2][2][5];   // [q][d4][d3]: row 4q + j, column col0 + 2 d3 + d4
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int d4 = 0; d4 < 2; ++d4) x[q][d4][k] = tile[4 * Lay::unit(col0 + 2 * k + d4) + j + PLANE * q];
+  if constexpr (TR) {
+    // inverse: transposed 2 x 2 blocks first, z[e] = sum_d G[d][e] x[d]
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        const float* G = &c.v[20 + 4 * k];
+        const float a = x[q][0][k], b = x[q][1][k];
+        x[q][0][k] = G[0] * a + G[2] * b;
+        x[q][1][k] = G[1] * a + G[3] * b;
+      }
+  }
+  // D[i][jj] = x[row 4q + i][(k, d4)] * C5[4h + jj][k]
+  f32x4 acc[2][2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int d4 = 0; d4 < 2; ++d4)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[q][d4][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][d4][0], c.v[(d4 * 2 + h) * 5], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                           0, 0, 0);
+#pragma unroll
+  for (int k = 1; k < 5; ++k)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int d4 = 0; d4 < 2; ++d4)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[q][d4][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][d4][k], c.v[(d4 * 2 + h) * 5 + k], acc[q][d4][h], 0, 0, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int o = 4 * h + j;   // this lane's radix-5 output
+    if (o < 5) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f32x4 z0 = acc[q][0][h], z1 = acc[q][1][h];
+        if constexpr (!TR) {
+          // forward: 2 x 2 block of column o on the pair (d4 = 0, 1)
+          const float* G = &c.v[20 + 4 * h];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = acc[q][0][h][i], b = acc[q][1][h][i];
+            z0[i] = G[0] * a + G[1] * b;
+            z1[i] = G[2] * a + G[3] * b;
+          }
+        }
+        *reinterpret_cast<f32x4*>(tile + 4 * Lay::unit(col0 + 2 * o) + PLANE * q) = z0;
+        *reinterpret_cast<f32x4*>(tile + 4 * Lay::unit(col0 + 2 * o + 1) + PLANE * q) = z1;
+      }
+    }
+  }
+}
+
+constexpr int k5CW = 8;                       // compute waves
+constexpr int k5IOW = 4;                      // data waves
+constexpr int k5Threads = 64 * (k5CW + k5IOW);
+
+// One radix-8 stage of the 5120 kernel (5 rounds, stride S, stage params sd),
+// coefficient buffers alternating; on exit the next stage's first round is in
+// the buffer given by the round parity.
+template <class Lay, int S, bool TR, typename TB, typename NextLoad>
+__device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, const StageFast& sd, Cbuf& X, Cbuf& Y,
+                                            int gb, int j, NextLoad next) {
+  using Sch = Sched<5120, Lay, List<St<8, S>>>;
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
+  // rounds 0..4: X holds round 0
+  load_coef<8, TB, TR>(rs, sd, 1 * kGPR, gb, j, as8(Y));
+  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 0 * kGPR + gb, as8(X), 0, 0, j);
+  load_coef<8, TB, TR>(rs, sd, 2 * kGPR, gb, j, as8(X));
+  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 1 * kGPR + gb, as8(Y), 0, 0, j);
+  load_coef<8, TB, TR>(rs, sd, 3 * kGPR, gb, j, as8(Y));
+  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 2 * kGPR + gb, as8(X), 0, 0, j);
+  load_coef<8, TB, TR>(rs, sd, 4 * kGPR, gb, j, as8(X));
+  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 3 * kGPR + gb, as8(Y), 0, 0, j);
+  next(Y);   // the next stage's round 0 goes to Y
+  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 4 * kGPR + gb, as8(X), 0, 0, j);
+  __syncthreads();
+}
+
+template <class Lay, bool TR, typename TB, typename NextLoad>
+__device__ __forceinline__ void stage_tail_5120(const RowParams& p, float* tile, const StageFast& s5,
+                                                const StageFast& s2, Cbuf& X, Cbuf& Y, int gb, int j,
+                                                NextLoad next) {
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
+  // rounds 0..3: X holds round 0
+  load_tail<TB, TR>(rs, s5, s2, 1 * kGPR, gb, j, Y);
+  tail_round<Lay, TR>(tile, 0 * kGPR + gb, X, j);
+  load_tail<TB, TR>(rs, s5, s2, 2 * kGPR, gb, j, X);
+  tail_round<Lay, TR>(tile, 1 * kGPR + gb, Y, j);
+  load_tail<TB, TR>(rs, s5, s2, 3 * kGPR, gb, j, Y);
+  tail_round<Lay, TR>(tile, 2 * kGPR + gb, X, j);
+  next(X);   // the next stage's round 0 goes to X
+  tail_round<Lay, TR>(tile, 3 * kGPR + gb, Y, j);
+  __syncthreads();
+}
+
+// Stage parameters p.st[] are in processing order: forward 640, 80, 10,
+// radix 5, radix 2; inverse radix 2, radix 5, 10, 80, 640.
+template <bool TR, typename T, typename TB>
+__global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
+  using Lay = LayXor;
+  extern __shared__ float tile[];
+  int64_t tix = blockIdx.x;
+  if (tix >= p.ntiles) return;   // uniform per workgroup
+  if (threadIdx.x >= 64 * k5CW) {
+    // 2 x 640 (bf16) or 2 x 1280 (fp32) micro-blocks over 256 data threads
+    constexpr bool F = std::is_same<T, float>::value;
+    data_waves_exact<T, Lay, 64 * k5IOW, F ? 10 : 5, F ? 4 : 5, 4, false>(p, tile, threadIdx.x - 64 * k5CW);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int gb = wave * 16 + (lane >> 2);
+  int j = lane & 3;
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
+  Cbuf ca, cb;
+  if constexpr (!TR) load_coef<8, TB, TR>(rs, p.st[0], 0, gb, j, as8(ca));
+  else load_tail<TB, TR>(rs, p.st[1], p.st[0], 0, gb, j, ca);
+  __syncthreads();
+  // The loop body covers two tiles: the first starts from ca, the second from
+  // cb (where the first tile's last stage leaves the next tile's first round).
+  // Every tile ends with the barrier after which the data waves have written
+  // the next tile, also the last one, so both roles pass the same barriers.
+  while (true) {
+    // keep per-round addresses inside the loop (hoisting them all out of it
+    // would exhaust the registers)
+    asm volatile("" : "+v"(gb), "+v"(j));
+    if constexpr (!TR) {
+      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[0], ca, cb, gb, j,
+                                    [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[1], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[1], cb, ca, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], ca, cb, gb, j,
+                                   [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[3], p.st[4], 0, gb, j, d); });
+      stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], cb, ca, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[0], 0, gb, j, as8(d)); });
+    } else {
+      stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], ca, cb, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], ca, cb, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[3], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[3], cb, ca, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[4], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], ca, cb, gb, j,
+                                    [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[1], p.st[0], 0, gb, j, d); });
+    }
+    __syncthreads();   // data waves have swapped the tile
+    tix += gridDim.x;
+    if (tix >= p.ntiles) break;
+    asm volatile("" : "+v"(gb), "+v"(j));
+    if constexpr (!TR) {
+      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[0], cb, ca, gb, j,
+                                    [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[1], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[1], ca, cb, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], cb, ca, gb, j,
+                                   [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[3], p.st[4], 0, gb, j, d); });
+      stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], ca, cb, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[0], 0, gb, j, as8(d)); });
+    } else {
+      stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], cb, ca, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], cb, ca, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[3], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[3], ca, cb, gb, j,
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[4], 0, gb, j, as8(d)); });
+      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], cb, ca, gb, j,
+                                    [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[1], p.st[0], 0, gb, j, d); });
+    }
+    __syncthreads();   // data waves have swapped the tile
+    tix += gridDim.x;
+    if (tix >= p.ntiles) break;
   }
 }
 
@@ -643,8 +852,19 @@ hipError_t launch_pair(const RowParams& p, int grid, hipStream_t st) {
 }
 
 template <typename T, typename TB>
+hipError_t launch_5120(const RowParams& p, int grid, hipStream_t st) {
+  void (*kern)(RowParams) = p.transpose ? apply_5120_kernel<true, T, TB> : apply_5120_kernel<false, T, TB>;
+  const size_t lds = (size_t)kRows * 4 * LayXor::units(5120);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(k5Threads), lds, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, typename TB>
 hipError_t launch_d(int d, const RowParams& p, int grid, hipStream_t st) {
-  return d == 4096 ? launch_pair<F4096, I4096, T, TB>(p, grid, st) : launch_pair<F5120, I5120, T, TB>(p, grid, st);
+  return d == 4096 ? launch_pair<F4096, I4096, T, TB>(p, grid, st) : launch_5120<T, TB>(p, grid, st);
 }
 
 }  // namespace

@@ -228,6 +228,105 @@ __device__ __forceinline__ void data_waves(const RowParams& p, float* tile, int 
   }
 }
 
+// Data waves with a fixed amount of memory work per tile.  The 2 x chunks
+// micro-blocks of a tile (row quad q, chunk c) are split evenly: data thread
+// it owns slots s = 0 .. NS-1, micro-block it + s * kIoT (the caller makes
+// 2 * chunks == NS * kIoT).  Slots 0 .. NP-1 of the next tile are prefetched
+// into registers while the compute waves run; the rest are loaded at the
+// swap, two at a time.  Rows past a ragged tile are clamped to its last row
+// (they hold that row's values), so every load and store is unconditional and
+// the waits count exactly.  Per tile the compute waves pass NB barriers (the
+// last one after their last stage); then each data thread, slot by slot,
+// stores its finished micro-block row by row (unless DOUT: the compute waves
+// stored the result) and writes the next tile's micro-block over it; the
+// stores are issued after every load the swap waits for except the later
+// slots' prefetches, so each wait counts them exactly.  One more barrier
+// releases the compute waves.
+template <typename T, class Lay, int kIoT, int NS, int NP, int NB, bool DOUT>
+__device__ __forceinline__ void data_waves_exact(const RowParams& p, float* tile, int it) {
+  constexpr int V = Io<T>::V;
+  static_assert(NP <= NS && (NS - NP) % 2 == 0, "synchronous slots go in pairs");
+  int64_t tix = blockIdx.x;
+  int qs[NS], cs[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int i = it + u * kIoT;
+    qs[u] = i >= p.chunks ? 1 : 0;
+    cs[u] = i - qs[u] * p.chunks;
+  }
+  {
+    const int nr = tile_rows(p, tix);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      IoBlock one;
+      io_load<T>(p, tix * kRows, nr, qs[u], cs[u], one);
+      io_to_lds<T, Lay>(p, tile, qs[u], cs[u], one);
+    }
+  }
+  __syncthreads();
+  IoBlock pf[NP > 0 ? NP : 1];
+  for (; tix < p.ntiles; tix += gridDim.x) {
+    // recompute the slot addresses every tile instead of keeping them all
+    // live across the loop
+#pragma unroll
+    for (int u = 0; u < NS; ++u) asm volatile("" : "+v"(qs[u]), "+v"(cs[u]));
+    const int64_t row0 = tix * kRows;
+    const int nr = tile_rows(p, tix);
+    const int64_t nxt = tix + gridDim.x;
+    const bool has_next = nxt < p.ntiles;
+    const int nr_next = has_next ? tile_rows(p, nxt) : 1;
+    uint2 osg[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      osg[u] = uint2{0u, 0u};
+      if (!DOUT && p.sign_mode == 2) {
+        const int8_t* sp = p.signs + cs[u] * V;
+        if constexpr (V == 8) osg[u] = *reinterpret_cast<const uint2*>(sp);
+        else osg[u].x = *reinterpret_cast<const uint32_t*>(sp);
+      }
+    }
+    if (has_next) {
+#pragma unroll
+      for (int u = 0; u < NP; ++u) io_load<T>(p, nxt * kRows, nr_next, qs[u], cs[u], pf[u]);
+    }
+#pragma unroll 1
+    for (int b = 0; b < NB; ++b) __syncthreads();
+    // one slot: read the finished micro-block, write the next one in its
+    // place, store the finished one
+    auto swap = [&](int u, const IoBlock& nb) {
+      if constexpr (!DOUT) {
+        T* y = static_cast<T*>(p.y);
+        const float* plane = tile + qs[u] * 4 * Lay::units(p.d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const uint32_t neg = (((e < 4 ? osg[u].x : osg[u].y) >> (8 * (e & 3))) & 0x80u) << 24;
+            v[e] = sgnf(plane[4 * Lay::unit(cs[u] * V + e) + i], neg);
+          }
+          const int r = 4 * qs[u] + i < nr ? 4 * qs[u] + i : nr - 1;
+          st_stream(y + (row0 + r) * p.ldy + (int64_t)cs[u] * V, pack_row<T>(v));
+        }
+      }
+      if (has_next) io_to_lds<T, Lay>(p, tile, qs[u], cs[u], nb);
+    };
+#pragma unroll
+    for (int u = 0; u < NP; ++u) swap(u, pf[u]);
+#pragma unroll
+    for (int u = NP; u < NS; u += 2) {
+      IoBlock a, b;
+      if (has_next) {
+        io_load<T>(p, nxt * kRows, nr_next, qs[u], cs[u], a);
+        io_load<T>(p, nxt * kRows, nr_next, qs[u + 1], cs[u + 1], b);
+      }
+      swap(u, a);
+      swap(u + 1, b);
+    }
+    __syncthreads();
+  }
+}
+
 // Host side: kernel parameters for rows of length pl.d (stages in processing
 // order, reversed for the inverse).
 inline RowParams make_row_params(const Plan& pl, bool inverse, const void* blocks, const float* scales,
