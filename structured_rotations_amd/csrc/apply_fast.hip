@@ -512,7 +512,8 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
   if (threadIdx.x >= 64 * kPCW) {
     // 2 x 512 (bf16) or 2 x 1024 (fp32) micro-blocks over 256 data threads
     constexpr bool F = std::is_same<T, float>::value;
-    data_waves_exact<T, typename Sch::Lay, 64 * kPIOW, F ? 8 : 4, 4, 2, DOUT>(p, tile, threadIdx.x - 64 * kPCW);
+    data_waves_exact<T, typename Sch::Lay, 64 * kPIOW, F ? 8 : 4, 4, 2, DOUT, false>(p, tile,
+                                                                                   threadIdx.x - 64 * kPCW);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -747,7 +748,7 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
   if (threadIdx.x >= 64 * k5CW) {
     // 2 x 640 (bf16) or 2 x 1280 (fp32) micro-blocks over 256 data threads
     constexpr bool F = std::is_same<T, float>::value;
-    data_waves_exact<T, Lay, 64 * k5IOW, F ? 10 : 5, F ? 4 : 5, 4, false>(p, tile, threadIdx.x - 64 * k5CW);
+    data_waves_exact<T, Lay, 64 * k5IOW, F ? 10 : 5, F ? 4 : 5, 4, false, true>(p, tile, threadIdx.x - 64 * k5CW);
     return;
   }
   const int lane = threadIdx.x & 63;

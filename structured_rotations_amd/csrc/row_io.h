@@ -242,7 +242,7 @@ __device__ __forceinline__ void data_waves(const RowParams& p, float* tile, int 
 // stores are issued after every load the swap waits for except the later
 // slots' prefetches, so each wait counts them exactly.  One more barrier
 // releases the compute waves.
-template <typename T, class Lay, int kIoT, int NS, int NP, int NB, bool DOUT>
+template <typename T, class Lay, int kIoT, int NS, int NP, int NB, bool DOUT, bool SPREAD>
 __device__ __forceinline__ void data_waves_exact(const RowParams& p, float* tile, int it) {
   constexpr int V = Io<T>::V;
   static_assert(NP <= NS && (NS - NP) % 2 == 0, "synchronous slots go in pairs");
@@ -285,12 +285,17 @@ __device__ __forceinline__ void data_waves_exact(const RowParams& p, float* tile
         else osg[u].x = *reinterpret_cast<const uint32_t*>(sp);
       }
     }
-    if (has_next) {
+    // SPREAD: the prefetch is spread over the stages (slot u goes out after
+    // barrier u * NB / NP), so that not a whole tile of loads sits in the
+    // vector cache's miss queue at once, in front of the compute waves'
+    // coefficient reads; otherwise it all goes out at the tile start.
 #pragma unroll
-      for (int u = 0; u < NP; ++u) io_load<T>(p, nxt * kRows, nr_next, qs[u], cs[u], pf[u]);
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int u = 0; u < NP; ++u)
+        if ((SPREAD ? u * NB / NP : 0) == b && has_next) io_load<T>(p, nxt * kRows, nr_next, qs[u], cs[u], pf[u]);
+      __syncthreads();
     }
-#pragma unroll 1
-    for (int b = 0; b < NB; ++b) __syncthreads();
     // one slot: read the finished micro-block, write the next one in its
     // place, store the finished one
     auto swap = [&](int u, const IoBlock& nb) {
