@@ -151,15 +151,25 @@ harp_status harp_rotate_weight(const harp_schedule* su, const void* blocks_u, co
   const DT io = static_cast<DT>(io_dtype);
   const DT bdt = static_cast<DT>(block_dtype);
   const bool inv = inverse != 0;
-  // Passes over the row index (U): runs of consecutive stages whose digits
-  // span at most 512 rows.
+  // Passes over the row index (U): runs of consecutive stages whose rows fit
+  // one LDS tile of 64 columns next to two coefficient slots (nsub rows x
+  // (64 + 2 x widest padded radix) floats in 160 KiB: 512 rows for radix 8).
   int cut[harp::kMaxStages + 1];
   int npass = 0;
   cut[0] = 0;
+  auto pad4 = [](int b) { return (b + 3) & ~3; };
   for (int t = 0; t < pu.m;) {
     int64_t prod = pu.radix[t];
+    int cw = pad4(pu.radix[t]) > 4 ? pad4(pu.radix[t]) : 4;
     int e = t + 1;
-    while (e < pu.m && prod * pu.radix[e] <= 512) prod *= pu.radix[e++];
+    while (e < pu.m) {
+      const int64_t np = prod * pu.radix[e];
+      const int cwn = pad4(pu.radix[e]) > cw ? pad4(pu.radix[e]) : cw;
+      if (np * (64 + 2 * cwn) > 40960) break;
+      prod = np;
+      cw = cwn;
+      ++e;
+    }
     cut[++npass] = e;
     t = e;
   }

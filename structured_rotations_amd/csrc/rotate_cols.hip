@@ -23,20 +23,25 @@ struct ColStage {
   int ls;        // stride of the digit inside the run's sub-index
   int blk_off;   // first coefficient of the stage
   int grp_off;   // first group of the stage
+  uint32_t mag_b, mag_bb;   // ceil(2^32 / b), ceil(2^32 / b^2) (see udiv)
+  uint32_t mag_ls;          // same for ls (0 for ls = 1)
+  int ncu;                  // coefficient slots per thread: ceil(nsub * b / 512)
 };
 
 struct ColParams {
   int nsub;          // rows per tile: product of the run's radices
   int nstage;        // stages in the run (processing order in st[])
   int pw;            // panel width (columns per tile)
+  int cslot;         // floats of one coefficient slot in LDS (nsub * widest padded row)
   int transpose;     // inverse: transposed blocks
-  int sign_mode;     // 0 none, 1 on load, 2 on store (indexed by row)
+  int sign_mode;     // 0 none, 1 on the input of the first stage, 2 on the output of the last
   int64_t suf;       // product of the radices after the run
   int64_t npanels;
   int64_t ntiles;    // (d / nsub) * npanels
   int64_t ncols;
-  int vec_in;        // 16-byte row segments: aligned base, ld and panel starts
-  int vec_out;
+  int vec;           // 16-byte row segments and whole panels: aligned bases, ld and widths
+  int dup;           // chunk slots wrap around (some chunks have two owners)
+  uint32_t mag_ncb;  // ceil(2^32 / (pw / 64)) (0 for one block)
   ColStage st[kMaxStagesDev];
   const void* blocks;
   const float* scales;
@@ -52,34 +57,100 @@ __device__ __forceinline__ float ld_el(const uint16_t* p) { return bf16_to_f32(*
 __device__ __forceinline__ void st_el(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st_el(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_rne(v); }
 
+// e / d for 0 <= e < 2^16 with mag = ceil(2^32 / d) (d >= 2), or mag = 0 for d = 1
+__device__ __forceinline__ int udiv(int e, uint32_t mag) { return mag ? (int)__umulhi((uint32_t)e, mag) : e; }
+
 // Row stride of a staged block in LDS: each output row of C starts on a
 // 16-byte boundary so a task reads it with 128-bit broadcast loads.
 template <int B>
 constexpr int coef_row_stride() { return (B + 3) & ~3; }
 
-// Stage the coefficients of the tile's groups for one stage into LDS as
-// fp32 C[o][k] (C = B forward, B^T inverse; int8 blocks dequantised), rows
-// padded to coef_row_stride<B>() floats, so the stage's tasks read them with
-// broadcast LDS loads.
-template <int B, typename TB>
-__device__ void stage_coefs(const ColParams& p, const ColStage& cs, float* cbuf, int64_t pre, int64_t q) {
-  constexpr int Bp = coef_row_stride<B>();
-  const int ngl = p.nsub / B;
-  const TB* blocks = static_cast<const TB*>(p.blocks) + cs.blk_off;
-  for (int e = threadIdx.x; e < ngl * B * B; e += blockDim.x) {
-    const int gl = e / (B * B);
-    const int i = e - gl * (B * B);
-    const int o = i / B, k = i - o * B;
-    const int64_t c = pre * (int64_t)ngl * p.suf + (int64_t)gl * p.suf + q;
-    float scale = 1.0f;
-    if constexpr (std::is_same<TB, int8_t>::value) scale = p.scales[cs.grp_off + c];
-    cbuf[gl * (B * Bp) + o * Bp + k] = coef<TB>(blocks, c * B * B + (p.transpose ? k * B + o : i), scale);
+// Tile geometry of one persistent-loop iteration.
+struct ColTile {
+  int64_t row_base;   // first row; tile row u is row_base + u * suf
+  int64_t col0;
+  int64_t pre, q;
+  int w;              // valid columns
+};
+
+__device__ __forceinline__ ColTile col_tile(const ColParams& p, int64_t tix) {
+  ColTile t;
+  const int64_t rt = tix / p.npanels;
+  const int64_t pn = tix - rt * p.npanels;
+  t.pre = rt / p.suf;
+  t.q = rt - t.pre * p.suf;
+  t.col0 = pn * p.pw;
+  const int64_t left = p.ncols - t.col0;
+  t.w = left < p.pw ? (int)left : p.pw;
+  t.row_base = t.pre * (int64_t)p.nsub * p.suf + t.q;
+  return t;
+}
+
+// Coefficients of one stage of one tile, fp32 C[o][k] (C = B forward, B^T
+// inverse; int8 blocks dequantised), with the signs folded in: the first
+// stage of a run with sign_mode 1 takes C[o][k] * s(row of input k), the last
+// one with sign_mode 2 takes s(row of output o) * C[o][k] -- the same
+// products as flipping the tile rows before or after, without touching the
+// data.  Thread t fetches elements e = t + u * 512 of the ngl * b * b (later
+// elements repeat the last one), NCU of them, into registers one stage ahead.
+template <typename TB, int NCU>
+__device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColTile& t, float (&cr)[NCU]) {
+  const ColStage& cs = p.st[s];
+  const int B = cs.b, BB = B * B, ngl = p.nsub / B;
+  const int n = ngl * BB;
+  const int ncu = cs.ncu;   // slots this stage needs (n <= 512 * ncu)
+  // group c = (pre * ngl + gl) * suf + q: uniform base plus gl * suf
+  const TB* blocks = static_cast<const TB*>(p.blocks) + cs.blk_off +
+                     (t.pre * (int64_t)ngl * p.suf + t.q) * BB;
+  const float* scales = p.scales + cs.grp_off + t.pre * (int64_t)ngl * p.suf + t.q;
+  const int8_t* signs = p.signs + t.row_base;
+  const bool sin = p.sign_mode == 1 && s == 0;
+  const bool sout = p.sign_mode == 2 && s == p.nstage - 1;
+  const int sufi = (int)p.suf;
+#pragma unroll
+  for (int u = 0; u < NCU; ++u) {
+    if (u < ncu) {
+      int e = threadIdx.x + u * 512;
+      e = e < n ? e : n - 1;
+      const int gl = udiv(e, cs.mag_bb);
+      const int i = e - gl * BB;
+      const int o = udiv(i, cs.mag_b);
+      const int k = i - o * B;
+      float scale = 1.0f;
+      if constexpr (std::is_same<TB, int8_t>::value) scale = scales[gl * sufi];
+      float v = coef<TB>(blocks, gl * sufi * BB + (p.transpose ? k * B + o : i), scale);
+      if (sin || sout) {
+        const int hi = udiv(gl, cs.mag_ls);
+        const int u_row = hi * B * cs.ls + (gl - hi * cs.ls) + (sin ? k : o) * cs.ls;
+        if (signs[u_row * sufi] < 0) v = -v;
+      }
+      cr[u] = v;
+    }
+  }
+}
+
+// Writes the fetched coefficients into a slot as C[gl][o][k] with rows padded
+// to 4 floats (the layout the stage tasks read).
+template <int NCU>
+__device__ __forceinline__ void coef_put(const ColParams& p, int s, const float (&cr)[NCU], float* slot) {
+  const ColStage& cs = p.st[s];
+  const int B = cs.b, BB = B * B, Bp = (B + 3) & ~3;
+  const int n = (p.nsub / B) * BB;
+#pragma unroll
+  for (int u = 0; u < NCU; ++u) {
+    const int e = threadIdx.x + u * 512;
+    if (u < cs.ncu && e < n) {
+      const int gl = udiv(e, cs.mag_bb);
+      const int i = e - gl * BB;
+      const int o = udiv(i, cs.mag_b);
+      slot[gl * (B * Bp) + o * Bp + (i - o * B)] = cr[u];
+    }
   }
 }
 
 // One stage of the run on the tile.  The tile is [nsub][pw] fp32; a task is
 // one group of the stage and a block of 64 columns, one column per lane, so
-// every lane of a wave uses the same coefficients (read from cbuf).  All
+// every lane of a wave uses the same coefficients (read from the slot).  All
 // reads of a task come before its stores (the tile and the coefficients
 // never overlap), so they are issued back to back.
 template <int B>
@@ -91,10 +162,10 @@ __device__ void col_stage(const ColParams& p, const ColStage& cs, float* __restr
   const int ntask = ngl * ncb;
   const int ls = cs.ls;
   for (int task = wave; task < ntask; task += nwaves) {
-    const int gl = task / ncb;
+    const int gl = udiv(task, p.mag_ncb);
     const int cb = task - gl * ncb;
-    const int u_lo = gl % ls;
-    const int u_hi = gl / ls;
+    const int u_hi = udiv(gl, cs.mag_ls);
+    const int u_lo = gl - u_hi * ls;
     const int ubase = u_hi * B * ls + u_lo;
     const f32x4* cf = reinterpret_cast<const f32x4*>(cbuf + gl * (B * Bp));
     float* col = tile + ubase * p.pw + cb * 64 + lane;
@@ -117,106 +188,88 @@ __device__ void col_stage(const ColParams& p, const ColStage& cs, float* __restr
   }
 }
 
+// The same stage on the matrix cores (radix <= 8): per task and output quad
+// h, v_mfma_f32_4x4x1f32 with A = C[4h + i][k] (i = lane & 3, read from the
+// slot as padded rows) and B = the lane's column value x[k]; lane 4b + j then
+// holds outputs 4h .. 4h+3 of its own column.  The coefficients reach the
+// lanes as four distinct rows per read instead of a broadcast of every value
+// to all 64 lanes, which is what bounds the vector-ALU form.
+template <int B>
+__device__ void col_stage_mfma(const ColParams& p, const ColStage& cs, float* __restrict__ tile,
+                               const float* __restrict__ cbuf, int wave, int nwaves, int lane) {
+  constexpr int Bp = coef_row_stride<B>();
+  constexpr int NH = (B + 3) / 4;
+  const int i = lane & 3;
+  const int ngl = p.nsub / B;
+  const int ncb = p.pw / 64;
+  const int ntask = ngl * ncb;
+  const int ls = cs.ls;
+  for (int task = wave; task < ntask; task += nwaves) {
+    const int gl = udiv(task, p.mag_ncb);
+    const int cb = task - gl * ncb;
+    const int u_hi = udiv(gl, cs.mag_ls);
+    const int u_lo = gl - u_hi * ls;
+    const int ubase = u_hi * B * ls + u_lo;
+    float* col = tile + ubase * p.pw + cb * 64 + lane;
+    float a[NH][Bp];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int o = 4 * h + i < B ? 4 * h + i : B - 1;   // rows past B: outputs dropped
+      const f32x4* row = reinterpret_cast<const f32x4*>(cbuf + gl * (B * Bp) + o * Bp);
+#pragma unroll
+      for (int c = 0; c < Bp / 4; ++c) {
+        const f32x4 q = row[c];
+        a[h][4 * c] = q.x; a[h][4 * c + 1] = q.y; a[h][4 * c + 2] = q.z; a[h][4 * c + 3] = q.w;
+      }
+    }
+    float v[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) v[k] = col[k * ls * p.pw];
+    f32x4 acc[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) acc[h] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[h][0], v[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int k = 1; k < B; ++k)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) acc[h] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[h][k], v[k], acc[h], 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        if (4 * h + ii < B) col[(4 * h + ii) * ls * p.pw] = acc[h][ii];
+  }
+}
+
 // BIG: radices 9..16 compiled in (their b^2 coefficients raise the
 // register count of the whole kernel, so runs of radices <= 8 use a kernel
 // without them).
-template <typename TB, bool BIG>
-__device__ void run_col_stage(const ColParams& p, int i, float* tile, float* cbuf, int64_t pre, int64_t q, int wave,
-                              int nwaves, int lane) {
-  const ColStage& cs = p.st[i];
+template <bool BIG>
+__device__ __forceinline__ void run_col_tasks(const ColParams& p, int s, float* tile, const float* slot, int wave,
+                                              int lane) {
+  const ColStage& cs = p.st[s];
   switch (cs.b) {
-    case 2:
-      stage_coefs<2, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<2>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 3:
-      stage_coefs<3, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<3>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 4:
-      stage_coefs<4, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<4>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 5:
-      stage_coefs<5, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<5>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 6:
-      stage_coefs<6, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<6>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 7:
-      stage_coefs<7, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<7>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 8:
-      stage_coefs<8, TB>(p, cs, cbuf, pre, q);
-      __syncthreads();
-      col_stage<8>(p, cs, tile, cbuf, wave, nwaves, lane);
-      break;
-    case 9:
+    case 2: col_stage_mfma<2>(p, cs, tile, slot, wave, 8, lane); break;
+    case 3: col_stage_mfma<3>(p, cs, tile, slot, wave, 8, lane); break;
+    case 4: col_stage_mfma<4>(p, cs, tile, slot, wave, 8, lane); break;
+    case 5: col_stage_mfma<5>(p, cs, tile, slot, wave, 8, lane); break;
+    case 6: col_stage_mfma<6>(p, cs, tile, slot, wave, 8, lane); break;
+    case 7: col_stage_mfma<7>(p, cs, tile, slot, wave, 8, lane); break;
+    case 8: col_stage_mfma<8>(p, cs, tile, slot, wave, 8, lane); break;
+    default:
       if constexpr (BIG) {
-        stage_coefs<9, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<9>(p, cs, tile, cbuf, wave, nwaves, lane);
+        switch (cs.b) {
+          case 9: col_stage<9>(p, cs, tile, slot, wave, 8, lane); break;
+          case 10: col_stage<10>(p, cs, tile, slot, wave, 8, lane); break;
+          case 11: col_stage<11>(p, cs, tile, slot, wave, 8, lane); break;
+          case 12: col_stage<12>(p, cs, tile, slot, wave, 8, lane); break;
+          case 13: col_stage<13>(p, cs, tile, slot, wave, 8, lane); break;
+          case 14: col_stage<14>(p, cs, tile, slot, wave, 8, lane); break;
+          case 15: col_stage<15>(p, cs, tile, slot, wave, 8, lane); break;
+          case 16: col_stage<16>(p, cs, tile, slot, wave, 8, lane); break;
+          default: break;
+        }
       }
       break;
-    case 10:
-      if constexpr (BIG) {
-        stage_coefs<10, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<10>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    case 11:
-      if constexpr (BIG) {
-        stage_coefs<11, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<11>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    case 12:
-      if constexpr (BIG) {
-        stage_coefs<12, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<12>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    case 13:
-      if constexpr (BIG) {
-        stage_coefs<13, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<13>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    case 14:
-      if constexpr (BIG) {
-        stage_coefs<14, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<14>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    case 15:
-      if constexpr (BIG) {
-        stage_coefs<15, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<15>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    case 16:
-      if constexpr (BIG) {
-        stage_coefs<16, TB>(p, cs, cbuf, pre, q);
-        __syncthreads();
-        col_stage<16>(p, cs, tile, cbuf, wave, nwaves, lane);
-      }
-      break;
-    default: break;
   }
 }
 
@@ -240,142 +293,182 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* v, float*) {
   return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
 }
 
-// Tile geometry of one persistent-loop iteration.
-struct ColTile {
-  int64_t row_base;   // first row; tile row u is row_base + u * suf
-  int64_t col0;
-  int64_t pre, q;
-  int w;              // valid columns
-};
-
-__device__ __forceinline__ ColTile col_tile(const ColParams& p, int64_t tix) {
-  ColTile t;
-  const int64_t rt = tix / p.npanels;
-  const int64_t pn = tix - rt * p.npanels;
-  t.pre = rt / p.suf;
-  t.q = rt - t.pre * p.suf;
-  t.col0 = pn * p.pw;
-  const int64_t left = p.ncols - t.col0;
-  t.w = left < p.pw ? (int)left : p.pw;
-  t.row_base = t.pre * (int64_t)p.nsub * p.suf + t.q;
-  return t;
+// Chunk slots of the 16-byte path: slot j of thread t is chunk t + 512 j of
+// the tile's nsub * pw / V; slots past the end wrap around to a chunk that
+// another slot also handles (it loads, writes and stores the same bytes), so
+// every thread issues exactly MAXC loads and stores per tile and the waits
+// before a prefetched tile goes into LDS count them exactly.
+__device__ __forceinline__ int chunk_of(int j, int total) {
+  const int i = (int)threadIdx.x + j * 512;
+  return i < total ? i : i % total;
 }
 
-// The tile's 16-byte input chunks owned by this thread (chunk i = threadIdx.x
-// + j * blockDim.x), loaded into registers ahead of use.
 template <typename TIN, int MAXC>
 __device__ __forceinline__ void col_prefetch(const ColParams& p, const ColTile& t, u32x4 (&r)[MAXC]) {
   constexpr int VI = ColIo<TIN>::V;
   const TIN* x = static_cast<const TIN*>(p.x);
   const int cpr = p.pw / VI;
+  const int total = p.nsub * cpr;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < p.nsub * cpr) {
-      const int u = i / cpr;
-      const int ch = i - u * cpr;
-      r[j] = ld_stream(x + (t.row_base + (int64_t)u * p.suf) * p.ldx + t.col0 + ch * VI);
-    }
+    const int i = chunk_of(j, total);
+    const int u = i / cpr;
+    const int ch = i - u * cpr;
+    r[j] = ld_stream(x + (t.row_base + (int64_t)u * p.suf) * p.ldx + t.col0 + ch * VI);
   }
 }
 
-template <typename TIN, int MAXC>
-__device__ __forceinline__ void col_to_lds(const ColParams& p, const ColTile& t, const u32x4 (&r)[MAXC], float* tile) {
-  constexpr int VI = ColIo<TIN>::V;
-  const int cpr = p.pw / VI;
-#pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < p.nsub * cpr) {
-      const int u = i / cpr;
-      const int ch = i - u * cpr;
-      float v[VI];
-      unpack_chunk(r[j], v, static_cast<const TIN*>(nullptr));
-      if (p.sign_mode == 1 && p.signs[t.row_base + (int64_t)u * p.suf] < 0) {
-#pragma unroll
-        for (int e = 0; e < VI; ++e) v[e] = -v[e];
-      }
-      float* dst = tile + u * p.pw + ch * VI;
-#pragma unroll
-      for (int e = 0; e < VI; e += 4) *reinterpret_cast<f32x4*>(dst + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
-    }
-  }
-}
-
-// MAXC: 16-byte input chunks per thread of a full tile (128 KiB of fp32 at
-// most: 8 for bf16 input, 16 for fp32 input, with 512 threads).
-template <typename TIN, typename TOUT, typename TB, bool BIG>
-__global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
-  extern __shared__ float tile[];
-  float* cbuf = tile + p.nsub * p.pw;     // one stage's coefficients (nsub * padded row floats)
+template <typename TIN, typename TOUT, int MAXC>
+__device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile& done, bool has_done, bool has_next,
+                                              const u32x4 (&r)[MAXC], float* tile) {
+  constexpr int V = ColIo<TIN>::V;
+  static_assert(ColIo<TIN>::V == ColIo<TOUT>::V || true, "");
   constexpr int VI = ColIo<TIN>::V, VO = ColIo<TOUT>::V;
-  constexpr int MAXC = VI == 8 ? 8 : 16;
-  const TIN* x = static_cast<const TIN*>(p.x);
+  static_assert(VI == VO || VI == 8 || VI == 4, "chunk widths");
+  (void)V;
   TOUT* y = static_cast<TOUT*>(p.y);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  // full tiles of a 16-byte aligned matrix stream through registers: the next
-  // tile's loads are in flight while this one is transformed and stored
-  const bool vec = p.vec_in && p.vec_out && p.ncols % p.pw == 0;
-  u32x4 pf[MAXC];
-  int64_t tix = blockIdx.x;
-  if (vec && tix < p.ntiles) col_prefetch<TIN, MAXC>(p, col_tile(p, tix), pf);
-  for (; tix < p.ntiles; tix += gridDim.x) {
-    const ColTile t = col_tile(p, tix);
-    if (vec) {
-      col_to_lds<TIN, MAXC>(p, t, pf, tile);
-      const int64_t nxt = tix + gridDim.x;
-      if (nxt < p.ntiles) col_prefetch<TIN, MAXC>(p, col_tile(p, nxt), pf);
-    } else {
-      for (int i = threadIdx.x; i < p.nsub * p.pw; i += blockDim.x) {
-        const int u = i / p.pw;
-        const int j = i - u * p.pw;
-        float v = 0.0f;
-        if (j < t.w) {
-          const int64_t row = t.row_base + (int64_t)u * p.suf;
-          v = ld_el(x + row * p.ldx + t.col0 + j);
-          if (p.sign_mode == 1 && p.signs[row] < 0) v = -v;
-        }
-        tile[i] = v;
-      }
-    }
-    __syncthreads();
-    for (int s = 0; s < p.nstage; ++s) {
-      run_col_stage<TB, BIG>(p, s, tile, cbuf, t.pre, t.q, wave, nwaves, lane);
-      __syncthreads();
-    }
-    if (vec) {
-      const int cpr = p.pw / VO;
-      for (int i = threadIdx.x; i < p.nsub * cpr; i += blockDim.x) {
-        const int u = i / cpr;
-        const int ch = i - u * cpr;
-        const int64_t row = t.row_base + (int64_t)u * p.suf;
-        const float* src = tile + u * p.pw + ch * VO;
+  const int cpr_i = p.pw / VI;
+  const int total = p.nsub * cpr_i;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    const int i = chunk_of(j, total);
+    const int u = i / cpr_i;
+    const int ch = i - u * cpr_i;
+    float* loc = tile + u * p.pw + ch * VI;
+    if (has_done) {
+      // VI / VO output chunks cover the same columns
+#pragma unroll
+      for (int h = 0; h < VI / VO; ++h) {
         float v[VO];
 #pragma unroll
         for (int e = 0; e < VO; e += 4) {
-          const f32x4 q4 = *reinterpret_cast<const f32x4*>(src + e);
+          const f32x4 q4 = *reinterpret_cast<const f32x4*>(loc + h * VO + e);
           v[e] = q4.x; v[e + 1] = q4.y; v[e + 2] = q4.z; v[e + 3] = q4.w;
         }
-        if (p.sign_mode == 2 && p.signs[row] < 0) {
-#pragma unroll
-          for (int e = 0; e < VO; ++e) v[e] = -v[e];
-        }
-        st_stream(y + row * p.ldy + t.col0 + ch * VO, pack_chunk(v, y));
+        st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI + h * VO,
+                  pack_chunk(v, static_cast<TOUT*>(nullptr)));
       }
-    } else {
-      for (int i = threadIdx.x; i < p.nsub * p.pw; i += blockDim.x) {
-        const int u = i / p.pw;
-        const int j = i - u * p.pw;
-        if (j < t.w) {
-          const int64_t row = t.row_base + (int64_t)u * p.suf;
-          float v = tile[i];
-          if (p.sign_mode == 2 && p.signs[row] < 0) v = -v;
-          st_el(y + row * p.ldy + t.col0 + j, v);
+      if constexpr (VO > VI) {
+        // fp32 in, bf16 out: pairs of input chunks make one output chunk;
+        // the even chunk of a pair stores both halves
+        static_assert(VO == 2 * VI, "chunk widths");
+        if ((ch & 1) == 0) {
+          float v[VO];
+#pragma unroll
+          for (int e = 0; e < VO; e += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(loc + e);
+            v[e] = q4.x; v[e + 1] = q4.y; v[e + 2] = q4.z; v[e + 3] = q4.w;
+          }
+          st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI,
+                    pack_chunk(v, static_cast<TOUT*>(nullptr)));
         }
       }
     }
+    if (has_next) {
+      float v[VI];
+      unpack_chunk(r[j], v, static_cast<const TIN*>(nullptr));
+#pragma unroll
+      for (int e = 0; e < VI; e += 4) *reinterpret_cast<f32x4*>(loc + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    }
+  }
+}
+
+// Slot by slot: store the finished tile's chunk (unless there is none yet),
+// then put the next tile's chunk in its place; the same thread owns both.
+// When slots wrap around (p.dup), a chunk has two owners, and one of them
+// could overwrite it before the other has stored it: then every store is
+// done first and a barrier separates them from the writes.
+template <typename TIN, typename TOUT, int MAXC>
+__device__ __forceinline__ void col_swap(const ColParams& p, const ColTile& done, bool has_done, bool has_next,
+                                         const u32x4 (&r)[MAXC], float* tile) {
+  if (p.dup) {
+    if (has_done) col_swap_part<TIN, TOUT, MAXC>(p, done, true, false, r, tile);
+    __syncthreads();
+    if (has_next) col_swap_part<TIN, TOUT, MAXC>(p, done, false, true, r, tile);
+  } else {
+    col_swap_part<TIN, TOUT, MAXC>(p, done, has_done, has_next, r, tile);
+  }
+}
+
+// Element path (unaligned matrices, ragged last panel): thread t owns
+// elements t + 512 k of the tile, for both the store and the load.
+template <typename TIN, typename TOUT>
+__device__ __forceinline__ void col_swap_el(const ColParams& p, const ColTile& done, bool has_done,
+                                            const ColTile& nt, bool has_next, float* tile) {
+  const TIN* x = static_cast<const TIN*>(p.x);
+  TOUT* y = static_cast<TOUT*>(p.y);
+  for (int i = threadIdx.x; i < p.nsub * p.pw; i += 512) {
+    const int u = i / p.pw;
+    const int j = i - u * p.pw;
+    if (has_done && j < done.w) st_el(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + j, tile[i]);
+    if (has_next) {
+      float v = 0.0f;
+      if (j < nt.w) v = ld_el(x + (nt.row_base + (int64_t)u * p.suf) * p.ldx + nt.col0 + j);
+      tile[i] = v;
+    }
+  }
+}
+
+// A pass over the tiles of one run.  Per tile: one barrier per stage; the
+// coefficients of the stage after the current one go into the other of two
+// LDS slots while the current stage runs (fetched into registers a stage
+// earlier, crossing into the next tile), and the finished tile is swapped
+// for the prefetched next one chunk by chunk after the last stage.  Every
+// thread issues the same global loads whatever the position in the pass
+// (past the last tile it re-reads the last one), so the waits count them
+// exactly and a stage never waits for the tile prefetch.
+template <typename TIN, typename TOUT, typename TB, bool BIG, bool VEC, int MAXC>
+__global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
+  constexpr int NCU = BIG ? 16 : 8;
+  extern __shared__ float tile[];
+  float* slots = tile + p.nsub * p.pw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t tix = blockIdx.x;
+  if (tix >= p.ntiles) return;   // uniform per workgroup
+  const int64_t last = p.ntiles - 1;
+  auto clampt = [&](int64_t x) { return x < p.ntiles ? x : last; };
+  ColTile t = col_tile(p, tix);
+  float cr[NCU];
+  // prologue: first tile and its first stage's coefficients in place
+  coef_fetch<TB, NCU>(p, 0, t, cr);
+  coef_put<NCU>(p, 0, cr, slots);
+  u32x4 pf[MAXC];
+  if constexpr (VEC) {
+    col_prefetch<TIN, MAXC>(p, t, pf);
+    col_swap<TIN, TOUT, MAXC>(p, t, false, true, pf, tile);
+  } else {
+    col_swap_el<TIN, TOUT>(p, t, false, t, true, tile);
+  }
+  // the stage after the current one: (sn, tixn)
+  int sn = 1;
+  int64_t tixn = tix;
+  if (sn == p.nstage) { sn = 0; tixn = tix + gridDim.x; }
+  coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cr);
+  if constexpr (VEC) col_prefetch<TIN, MAXC>(p, col_tile(p, clampt(tix + gridDim.x)), pf);
+  __syncthreads();
+  int slot = 0;
+  while (true) {
+    for (int s = 0; s < p.nstage; ++s) {
+      // coefficients of the next stage into the other slot, then fetch the
+      // one after
+      if (tixn < p.ntiles) coef_put<NCU>(p, sn, cr, slots + (slot ^ 1) * p.cslot);
+      ++sn;
+      if (sn == p.nstage) { sn = 0; tixn += gridDim.x; }
+      coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cr);
+      run_col_tasks<BIG>(p, s, tile, slots + slot * p.cslot, wave, lane);
+      __syncthreads();
+      slot ^= 1;
+    }
+    const int64_t tnx = tix + gridDim.x;
+    const bool has_next = tnx < p.ntiles;
+    const ColTile nt = col_tile(p, clampt(tnx));
+    if constexpr (VEC) col_swap<TIN, TOUT, MAXC>(p, t, true, has_next, pf, tile);
+    else col_swap_el<TIN, TOUT>(p, t, true, nt, has_next, tile);
+    if (!has_next) break;
+    tix = tnx;
+    t = nt;
+    if constexpr (VEC) col_prefetch<TIN, MAXC>(p, col_tile(p, clampt(tix + gridDim.x)), pf);
     __syncthreads();
   }
 }
@@ -394,9 +487,17 @@ int cus_for_cols() {
   return cus;
 }
 
-template <typename TIN, typename TOUT, typename TB>
-hipError_t launch_cols_typed(const ColParams& p, bool big, int grid, size_t lds, hipStream_t st) {
-  auto kern = big ? col_pass_kernel<TIN, TOUT, TB, true> : col_pass_kernel<TIN, TOUT, TB, false>;
+// MAXC: 16-byte chunks per thread and tile; two sizes per input type (the
+// smaller one for short tiles), anything larger takes the element path.
+template <typename TIN> struct ColMaxc;
+template <> struct ColMaxc<uint16_t> { static constexpr int lo = 4, hi = 8; };
+template <> struct ColMaxc<float> { static constexpr int lo = 8, hi = 16; };
+
+template <typename TIN, typename TOUT, typename TB, bool BIG>
+hipError_t launch_cols_k(const ColParams& p, int maxc, int grid, size_t lds, hipStream_t st) {
+  void (*kern)(ColParams) = !p.vec                      ? col_pass_kernel<TIN, TOUT, TB, BIG, false, 1>
+                            : maxc <= ColMaxc<TIN>::lo ? col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::lo>
+                                                       : col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::hi>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -405,11 +506,17 @@ hipError_t launch_cols_typed(const ColParams& p, bool big, int grid, size_t lds,
 }
 
 template <typename TIN, typename TOUT>
-hipError_t launch_cols_blk(DT bdt, const ColParams& p, bool big, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_cols_blk(DT bdt, const ColParams& p, bool big, int maxc, int grid, size_t lds, hipStream_t st) {
   switch (bdt) {
-    case DT::F32: return launch_cols_typed<TIN, TOUT, float>(p, big, grid, lds, st);
-    case DT::BF16: return launch_cols_typed<TIN, TOUT, uint16_t>(p, big, grid, lds, st);
-    case DT::I8: return launch_cols_typed<TIN, TOUT, int8_t>(p, big, grid, lds, st);
+    case DT::F32:
+      return big ? launch_cols_k<TIN, TOUT, float, true>(p, maxc, grid, lds, st)
+                 : launch_cols_k<TIN, TOUT, float, false>(p, maxc, grid, lds, st);
+    case DT::BF16:
+      return big ? launch_cols_k<TIN, TOUT, uint16_t, true>(p, maxc, grid, lds, st)
+                 : launch_cols_k<TIN, TOUT, uint16_t, false>(p, maxc, grid, lds, st);
+    case DT::I8:
+      return big ? launch_cols_k<TIN, TOUT, int8_t, true>(p, maxc, grid, lds, st)
+                 : launch_cols_k<TIN, TOUT, int8_t, false>(p, maxc, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -428,45 +535,72 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   p.suf = pl.stride[t1 - 1];
   p.transpose = inverse ? 1 : 0;
   p.sign_mode = signs ? sign_mode : 0;
+  auto mag = [](int d) { return d == 1 ? 0u : (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d); };
+  int bmax = 2, cw = 4;   // largest radix; widest padded coefficient row
   for (int i = 0; i < p.nstage; ++i) {
     const int t = inverse ? t1 - 1 - i : t0 + i;
-    p.st[i].b = pl.radix[t];
-    p.st[i].ls = (int)(pl.stride[t] / p.suf);
-    p.st[i].blk_off = (int)pl.blk_off[t];
-    p.st[i].grp_off = (int)pl.grp_off[t];
+    ColStage& cs = p.st[i];
+    cs.b = pl.radix[t];
+    cs.ls = (int)(pl.stride[t] / p.suf);
+    cs.blk_off = (int)pl.blk_off[t];
+    cs.grp_off = (int)pl.grp_off[t];
+    cs.mag_b = mag(cs.b);
+    cs.mag_bb = mag(cs.b * cs.b);
+    cs.mag_ls = mag(cs.ls);
+    cs.ncu = (nsub * cs.b + 511) / 512;
+    bmax = cs.b > bmax ? cs.b : bmax;
+    cw = ((cs.b + 3) & ~3) > cw ? ((cs.b + 3) & ~3) : cw;
   }
+  // A stage stages nsub * b coefficients per thread block of 512 threads:
+  // at most 8 (radix <= 8) or 16 per thread.
+  const bool big = bmax > 8;
+  if ((size_t)nsub * bmax > (size_t)512 * (big ? 16 : 8)) return hipErrorInvalidValue;
   // Panel width: the widest multiple of 64 columns (at most 512) whose fp32
-  // tile fits in 128 KiB; stage tasks are 64-column blocks, so a run wider
-  // than 512 rows is not supported here (the host splits runs at 512).
-  int pw = 512;
-  while (pw > 64 && (size_t)nsub * pw * sizeof(float) > (size_t)128 * 1024) pw -= 64;
-  if ((size_t)nsub * (pw + 16) * sizeof(float) > (size_t)160 * 1024) return hipErrorInvalidValue;
+  // tile plus two coefficient slots fit in 160 KiB (stage tasks are 64-column
+  // blocks).
+  p.cslot = nsub * cw;
+  // Panel width: a multiple of 64 columns (stage tasks are 64-column blocks)
+  // up to 1024, as wide as fits next to two coefficient slots in 80 KiB (two
+  // workgroups per CU) or, failing that, in 160 KiB; among those the widest
+  // that divides the column count (whole panels take the 16-byte path).
+  auto fits = [&](int w, size_t cap) { return (size_t)nsub * (w + 2 * cw) * sizeof(float) <= cap; };
+  const size_t cap = fits(256, (size_t)80 * 1024) ? (size_t)80 * 1024 : (size_t)160 * 1024;
+  int pw = 0, pw_div = 0;
+  for (int w = 64; w <= 1024; w += 64) {
+    if (!fits(w, cap)) break;
+    pw = w;
+    if (ncols % w == 0) pw_div = w;
+  }
+  if (pw == 0) return hipErrorInvalidValue;
+  if (pw_div >= pw / 2) pw = pw_div;
   p.pw = pw;
+  p.mag_ncb = mag(pw / 64);
   p.ncols = ncols;
   p.npanels = (ncols + pw - 1) / pw;
   p.ntiles = (pl.d / nsub) * p.npanels;
   p.blocks = blocks;
   p.scales = scales;
-  p.signs = signs;
+  // without signs the kernel still reads a (discarded) byte: point at the blocks
+  p.signs = signs ? signs : static_cast<const int8_t*>(blocks);
   p.x = x;
   p.ldx = ldx;
   p.y = y;
   p.ldy = ldy;
   const int ib = io_bytes(in_dt), ob = io_bytes(out_dt);
-  p.vec_in = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (ldx * ib) % 16 == 0;
-  p.vec_out = reinterpret_cast<uintptr_t>(y) % 16 == 0 && (ldy * ob) % 16 == 0;
-  int bmax = 2, cw = 4;   // largest radix; widest padded coefficient row (a stage stages nsub * row floats)
-  for (int t = t0; t < t1; ++t) {
-    bmax = pl.radix[t] > bmax ? pl.radix[t] : bmax;
-    cw = ((pl.radix[t] + 3) & ~3) > cw ? ((pl.radix[t] + 3) & ~3) : cw;
-  }
-  const size_t lds = ((size_t)nsub * pw + (size_t)nsub * cw) * sizeof(float);
+  const int vi = 16 / ib;
+  const int maxc = (int)(((int64_t)nsub * (pw / vi) + 511) / 512);
+  const int maxc_cap = in_dt == DT::F32 ? 16 : 8;
+  p.vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (ldx * ib) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0 &&
+          (ldy * ob) % 16 == 0 && ncols % pw == 0 && maxc <= maxc_cap && !(in_dt == DT::F32 && out_dt == DT::BF16);
+  p.dup = (int64_t)(maxc <= (in_dt == DT::F32 ? 8 : 4) ? (in_dt == DT::F32 ? 8 : 4) : maxc_cap) * 512 !=
+          (int64_t)nsub * (pw / vi);
+  const size_t lds = ((size_t)nsub * pw + (size_t)2 * p.cslot) * sizeof(float);
   int64_t grid = (int64_t)cus_for_cols() * (lds > 80 * 1024 ? 1 : 2);
   if (grid > p.ntiles) grid = p.ntiles;
-  if (in_dt == DT::F32 && out_dt == DT::F32) return launch_cols_blk<float, float>(bdt, p, bmax > 8, (int)grid, lds, stream);
-  if (in_dt == DT::BF16 && out_dt == DT::BF16) return launch_cols_blk<uint16_t, uint16_t>(bdt, p, bmax > 8, (int)grid, lds, stream);
-  if (in_dt == DT::BF16 && out_dt == DT::F32) return launch_cols_blk<uint16_t, float>(bdt, p, bmax > 8, (int)grid, lds, stream);
-  if (in_dt == DT::F32 && out_dt == DT::BF16) return launch_cols_blk<float, uint16_t>(bdt, p, bmax > 8, (int)grid, lds, stream);
+  if (in_dt == DT::F32 && out_dt == DT::F32) return launch_cols_blk<float, float>(bdt, p, big, maxc, (int)grid, lds, stream);
+  if (in_dt == DT::BF16 && out_dt == DT::BF16) return launch_cols_blk<uint16_t, uint16_t>(bdt, p, big, maxc, (int)grid, lds, stream);
+  if (in_dt == DT::BF16 && out_dt == DT::F32) return launch_cols_blk<uint16_t, float>(bdt, p, big, maxc, (int)grid, lds, stream);
+  if (in_dt == DT::F32 && out_dt == DT::BF16) return launch_cols_blk<float, uint16_t>(bdt, p, big, maxc, (int)grid, lds, stream);
   return hipErrorInvalidValue;
 }
 
