@@ -1,26 +1,21 @@
-// Schedule-specialised matrix-core row kernel for the HARP transform.
+// Schedule-specialised matrix-core row kernels for the HARP transform.
 //
 // HARP technical summary (gist.science 2605.29843), §2.1/§2.2: stage t
 // applies, to every group of coordinates that agree on all digits but digit
-// t, its own b_t x b_t orthogonal block.  This kernel computes exactly what
-// the generic matrix-core kernel computes (same 8-row tile, same
-// v_mfma_f32_4x4x1f32 mapping: a block of 4 lanes owns one group, lane j
-// supplies row j's input and coefficient row 4h+j), but for schedules known
-// at compile time, so that the per-round work is almost only matrix-core
-// instructions and LDS accesses:
-//   * every stage's radix and digit stride are constants: group -> column
-//     arithmetic folds, and the next stage's coefficient load needs no
-//     radix dispatch;
-//   * with the padded layout (one spare unit per 8 columns) the B inputs of
-//     a group sit at base + constant(k), so each round computes one LDS
-//     address and the rest are immediate offsets (checked at compile time);
-//   * coefficient registers alternate between two buffers from round to
-//     round (loaded one round ahead, into the buffer the previous round has
-//     finished with) instead of being copied;
-//   * coefficient loads are unconditional (rows past the radix re-read the
-//     last row; those outputs are never written), so nothing is zero-filled.
-// Data waves, signs and the direct store of a contiguous last stage are as
-// in the generic kernel.
+// t, its own b_t x b_t orthogonal block.  These kernels compute what the
+// generic matrix-core kernel computes (8-row tiles in LDS, data waves that
+// stream tiles in and out, v_mfma_f32_4x4x1f32 with a block of 4 lanes per
+// group and lane j carrying row j of a row quad), for two schedules known at
+// compile time:
+//   * d = 4096, (8,8,8,8): 16 rounds of 16 groups per compute wave; the
+//     padded LDS layout makes every gather an immediate offset; coefficients
+//     come through a buffer resource three rounds ahead into four rotating
+//     register buffers; rounds are ordered so no LDS latency lands on the
+//     matrix cores; wave-local group sets leave one exchange barrier per
+//     tile; the last stage stores straight to HBM.
+//   * d = 5120, (8,8,8,5,2): three radix-8 stages and one fused stage for the
+//     radix-5 / radix-2 pair, whose digits both lie inside 10 consecutive
+//     columns (4 rounds instead of 28).
 #include <type_traits>
 
 #include "row_io.h"
@@ -32,9 +27,7 @@ namespace {
 using namespace rowk;
 
 constexpr int kCW = 8;                    // compute waves
-constexpr int kIOW = 8;                   // data waves
-constexpr int kGPR = 16 * kCW;            // groups per round
-constexpr int kThreads = 64 * (kCW + kIOW);
+constexpr int kGPR = 16 * kCW;            // groups per round (16 per compute wave)
 
 template <int B_, int S_>
 struct St {
@@ -81,16 +74,6 @@ constexpr bool linear_stage() {
       if (Lay::unit(c0 + k * S) - Lay::unit(c0) != Lay::unit(k * S) - Lay::unit(0)) return false;
   }
   return true;
-}
-
-template <class Sch, int I>
-constexpr int rounds_before() {
-  if constexpr (I == 0) {
-    return 0;
-  } else {
-    using Sp = typename At<I - 1, typename Sch::L>::type;
-    return rounds_before<Sch, I - 1>() + Sch::D / Sp::B / kGPR;
-  }
 }
 
 template <class Sch, int I = 0>
@@ -224,96 +207,6 @@ __device__ __forceinline__ void round_compute(const RowParams& p, float* tile, i
           st_stream(y + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
         }
       }
-    }
-  }
-}
-
-// Stage I of the schedule over the tile.  SW selects which coefficient buffer
-// holds round 0 (loaded by the previous stage); on exit the next stage's round
-// 0 (after the last stage: the next tile's) is in the buffer the next stage
-// expects, which is compile-time known from the round counts.
-template <class Sch, int I, bool SW, bool TR, bool DOUT, typename T, typename TB>
-__device__ __forceinline__ void run_stage(const RowParams& p, float* tile, float (&ca)[2][8], float (&cb)[2][8], int gb,
-                                          int j, int64_t row0, int nr) {
-  constexpr int M = Sch::M;
-  using Sg = typename At<I, typename Sch::L>::type;
-  using Sn = typename At<(I + 1) % M, typename Sch::L>::type;
-  constexpr int B = Sg::B, S = Sg::S, R = Sch::D / B / kGPR;
-  constexpr bool DIRECT = DOUT && I == M - 1;
-  static_assert(!DIRECT || (B == 8 && S == 1), "direct store needs a contiguous radix-8 last stage");
-  float(&X)[2][8] = SW ? cb : ca;
-  float(&Y)[2][8] = SW ? ca : cb;
-  const StageFast& sd = p.st[I];
-  const StageFast& sn = p.st[(I + 1) % M];
-  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
-  if constexpr (R % 2 == 0) {
-#pragma unroll 1
-    for (int r = 0; r < R - 2; r += 2) {
-      load_coef<B, TB, TR>(rs, sd, (r + 1) * kGPR, gb, j, Y);
-      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, r * kGPR + gb, X, row0, nr, j);
-      load_coef<B, TB, TR>(rs, sd, (r + 2) * kGPR, gb, j, X);
-      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (r + 1) * kGPR + gb, Y, row0, nr, j);
-    }
-    load_coef<B, TB, TR>(rs, sd, (R - 1) * kGPR, gb, j, Y);
-    round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 2) * kGPR + gb, X, row0, nr, j);
-    load_coef<Sn::B, TB, TR>(rs, sn, 0, gb, j, X);
-    round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 1) * kGPR + gb, Y, row0, nr, j);
-  } else {
-#pragma unroll 1
-    for (int r = 0; r < R - 1; r += 2) {
-      load_coef<B, TB, TR>(rs, sd, (r + 1) * kGPR, gb, j, Y);
-      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, r * kGPR + gb, X, row0, nr, j);
-      load_coef<B, TB, TR>(rs, sd, (r + 2) * kGPR, gb, j, X);
-      round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (r + 1) * kGPR + gb, Y, row0, nr, j);
-    }
-    load_coef<Sn::B, TB, TR>(rs, sn, 0, gb, j, Y);
-    round_compute<Sch, B, S, TR, DIRECT, T>(p, tile, (R - 1) * kGPR + gb, X, row0, nr, j);
-  }
-  __syncthreads();
-  if constexpr (I + 1 < M) {
-    constexpr bool SW2 = (R % 2 == 0) ? SW : !SW;
-    run_stage<Sch, I + 1, SW2, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, row0, nr);
-  }
-}
-
-template <class Sch, bool SW, bool TR, bool DOUT, typename T, typename TB>
-__device__ __forceinline__ void tile_body(const RowParams& p, float* tile, float (&ca)[2][8], float (&cb)[2][8],
-                                          int gb, int j, int64_t tix) {
-  const int64_t row0 = tix * kRows;
-  const int nr = tile_rows(p, tix);
-  run_stage<Sch, 0, SW, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, row0, nr);
-  if (!DOUT) __syncthreads();   // data waves copy the tile out
-  __syncthreads();              // data waves write the next tile in
-}
-
-template <class Sch, bool TR, bool DOUT, typename T, typename TB>
-__global__ void __launch_bounds__(kThreads) apply_fast_kernel(RowParams p) {
-  constexpr int RT = rounds_before<Sch, Sch::M>();   // rounds per tile
-  extern __shared__ float tile[];
-  int64_t tix = blockIdx.x;
-  if (tix >= p.ntiles) return;   // uniform per workgroup
-  if (threadIdx.x >= 64 * kCW) {
-    data_waves<T, 64 * kIOW, 1, typename Sch::Lay>(p, tile, threadIdx.x - 64 * kCW);
-    return;
-  }
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int gb = wave * 16 + (lane >> 2);
-  const int j = lane & 3;
-  float ca[2][8], cb[2][8];
-  using S0 = typename At<0, typename Sch::L>::type;
-  load_coef<S0::B, TB, TR>(coef_rsrc(p), p.st[0], 0, gb, j, ca);
-  __syncthreads();
-  while (true) {
-    tile_body<Sch, false, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, tix);
-    tix += gridDim.x;
-    if (tix >= p.ntiles) break;
-    if constexpr (RT % 2 == 1) {
-      // an odd number of rounds per tile leaves the next tile's first
-      // coefficients in the other buffer
-      tile_body<Sch, true, TR, DOUT, T, TB>(p, tile, ca, cb, gb, j, tix);
-      tix += gridDim.x;
-      if (tix >= p.ntiles) break;
     }
   }
 }
@@ -821,8 +714,6 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
 // the 160 KiB LDS exactly and keeps the unpadded XOR layout.
 using F4096 = Sched<4096, LayPad8, List<St<8, 512>, St<8, 64>, St<8, 8>, St<8, 1>>>;
 using I4096 = Sched<4096, LayPad8, List<St<8, 1>, St<8, 8>, St<8, 64>, St<8, 512>>>;
-using F5120 = Sched<5120, LayXor, List<St<8, 640>, St<8, 80>, St<8, 10>, St<5, 2>, St<2, 1>>>;
-using I5120 = Sched<5120, LayXor, List<St<2, 1>, St<5, 2>, St<8, 10>, St<8, 80>, St<8, 640>>>;
 
 static_assert(linear_stage<LayPad8, 4096, 8, 512>() && linear_stage<LayPad8, 4096, 8, 64>() &&
                   linear_stage<LayPad8, 4096, 8, 8>() && linear_stage<LayPad8, 4096, 8, 1>(),
@@ -830,15 +721,12 @@ static_assert(linear_stage<LayPad8, 4096, 8, 512>() && linear_stage<LayPad8, 409
 
 template <class Sch, bool TR, bool DOUT, typename T, typename TB>
 hipError_t launch_sched(const RowParams& p, int grid, hipStream_t st) {
-  constexpr bool PIPE = rounds_before_rt<Sch>(Sch::M) % 4 == 0;
-  void (*kern)(RowParams);
-  if constexpr (PIPE) kern = apply_pipe_kernel<Sch, TR, DOUT, T, TB>;
-  else kern = apply_fast_kernel<Sch, TR, DOUT, T, TB>;
+  void (*kern)(RowParams) = apply_pipe_kernel<Sch, TR, DOUT, T, TB>;
   const size_t lds = (size_t)kRows * 4 * Sch::Lay::units(Sch::D);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(PIPE ? kPThreads : kThreads), lds, st, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kPThreads), lds, st, p);
   return hipGetLastError();
 }
 

@@ -294,13 +294,15 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* v, float*) {
 }
 
 // Chunk slots of the 16-byte path: slot j of thread t is chunk t + 512 j of
-// the tile's nsub * pw / V; slots past the end wrap around to a chunk that
-// another slot also handles (it loads, writes and stores the same bytes), so
-// every thread issues exactly MAXC loads and stores per tile and the waits
-// before a prefetched tile goes into LDS count them exactly.
+// the tile's nsub * pw / V.  A slot past the end repeats the thread's own
+// slot-0 chunk (it loads the same bytes, writes them to LDS again and stores
+// slot 0's finished data again), so every thread issues exactly MAXC loads
+// and stores per tile and the waits before a prefetched tile goes into LDS
+// count them exactly.  With fewer than 512 chunks a thread may have no chunk
+// of its own: then the slot wraps to another thread's chunk (p.dup).
 __device__ __forceinline__ int chunk_of(int j, int total) {
   const int i = (int)threadIdx.x + j * 512;
-  return i < total ? i : i % total;
+  return i < total ? i : (total >= 512 ? (int)threadIdx.x : i % total);
 }
 
 template <typename TIN, int MAXC>
@@ -329,9 +331,12 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
   TOUT* y = static_cast<TOUT*>(p.y);
   const int cpr_i = p.pw / VI;
   const int total = p.nsub * cpr_i;
+  constexpr int NO = VI / VO > 0 ? VI / VO : 1;
+  u32x4 keep[NO];   // slot 0's finished data, stored again by repeated slots
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
     const int i = chunk_of(j, total);
+    const bool rep = j > 0 && total >= 512 && (int)threadIdx.x + j * 512 >= total;
     const int u = i / cpr_i;
     const int ch = i - u * cpr_i;
     float* loc = tile + u * p.pw + ch * VI;
@@ -345,8 +350,10 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
           const f32x4 q4 = *reinterpret_cast<const f32x4*>(loc + h * VO + e);
           v[e] = q4.x; v[e + 1] = q4.y; v[e + 2] = q4.z; v[e + 3] = q4.w;
         }
-        st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI + h * VO,
-                  pack_chunk(v, static_cast<TOUT*>(nullptr)));
+        u32x4 o = pack_chunk(v, static_cast<TOUT*>(nullptr));
+        if (j == 0) keep[h] = o;
+        else if (rep) o = keep[h];
+        st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI + h * VO, o);
       }
       if constexpr (VO > VI) {
         // fp32 in, bf16 out: pairs of input chunks make one output chunk;
@@ -375,9 +382,10 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
 
 // Slot by slot: store the finished tile's chunk (unless there is none yet),
 // then put the next tile's chunk in its place; the same thread owns both.
-// When slots wrap around (p.dup), a chunk has two owners, and one of them
-// could overwrite it before the other has stored it: then every store is
-// done first and a barrier separates them from the writes.
+// When slots wrap around to other threads' chunks (p.dup), a chunk has two
+// owners, and one of them could overwrite it before the other has stored it:
+// then every store is done first and a barrier separates them from the
+// writes.
 template <typename TIN, typename TOUT, int MAXC>
 __device__ __forceinline__ void col_swap(const ColParams& p, const ColTile& done, bool has_done, bool has_next,
                                          const u32x4 (&r)[MAXC], float* tile) {
@@ -592,8 +600,7 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   const int maxc_cap = in_dt == DT::F32 ? 16 : 8;
   p.vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (ldx * ib) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0 &&
           (ldy * ob) % 16 == 0 && ncols % pw == 0 && maxc <= maxc_cap && !(in_dt == DT::F32 && out_dt == DT::BF16);
-  p.dup = (int64_t)(maxc <= (in_dt == DT::F32 ? 8 : 4) ? (in_dt == DT::F32 ? 8 : 4) : maxc_cap) * 512 !=
-          (int64_t)nsub * (pw / vi);
+  p.dup = (int64_t)nsub * (pw / vi) < 512;
   const size_t lds = ((size_t)nsub * pw + (size_t)2 * p.cslot) * sizeof(float);
   int64_t grid = (int64_t)cus_for_cols() * (lds > 80 * 1024 ? 1 : 2);
   if (grid > p.ntiles) grid = p.ntiles;
