@@ -193,7 +193,8 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
   // schedule has one, else the matrix-core kernel for fp32 and bf16 blocks
   // and the vector-ALU kernel for int8 blocks (whose coefficient traffic is
   // small enough that the plain FMA path wins).  HARP_ROW_KERNEL overrides
-  // the choice (1 matrix-core, 2 vector-ALU, 3 generic tile kernel);
+  // the choice (1 generic matrix-core, 2 vector-ALU, 3 generic tile kernel,
+  // 4 schedule-specialised kernels where they apply);
   // HARP_ROW_ROLES picks the matrix-core kernel's wave split.
   static const int row_kernel = env_int("HARP_ROW_KERNEL", 0);
   if (in_dt == out_dt && row_kernel != 3 && row_path_supported(pl, in_dt, blocks, signs, x, ldx, y, ldy)) {
