@@ -1,6 +1,8 @@
 """Benchmark of the HARP apply path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--blk f32|bf16|i8]
+    python bench.py --mode latency [--workload NAME] [--blk ...]
+    python bench.py --mode materialize [--workload NAME]
 
 A step is one pass of the hot path over one batch: for the default workload
 (cayley4096_bf16: 16384 rows x 4096, bf16 rows, schedule (8,8,8,8), Cayley
@@ -13,6 +15,17 @@ device synchronisation).  roofline.achieved = algorithmic bytes per launch
 (rows * d * 2 bytes read + rows * d * 2 bytes written) / the kernel's mean
 duration, measured with HIP events recorded on the stream the kernel runs on.
 cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
+
+--mode latency: the per-token (decode) regime, 1 to 64 rows per call.  For
+each row count: microseconds per call of K back-to-back calls issued from
+Python (host launch cost included), and of the same calls captured once in a
+HIP graph and replayed (device time per call, launch gaps included), with the
+output of the graph replay checked against eager calls and, for some rows,
+against the oracle.
+
+--mode materialize: microseconds per call of the block materialisation on the
+device from fp64 parameters and from int8 parameter codes, and of the int8
+quantisation of the parameters (setup work, not part of a step).
 """
 from __future__ import annotations
 
@@ -96,6 +109,165 @@ def cpu_baseline(w: dict, blk: str, budget_s: float = 30.0) -> dict:
                 "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread"}
 
 
+LAT_ROWS = (1, 2, 4, 8, 16, 32, 64)
+
+
+def latency_main(args) -> int:
+    """Decode regime: microseconds per harp_apply call at 1-64 rows."""
+    import torch
+
+    from oracle import harp_oracle as O
+    from structured_rotations_amd import api
+    from structured_rotations_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    w = W.make(name, rows=max(LAT_ROWS))
+    d, sch, io = w["d"], w["schedule"], w["io"]
+    if w["workload"].kind != "apply":
+        print("--mode latency runs an apply workload", file=sys.stderr)
+        return 2
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    th = torch.from_numpy(w["theta"]).cuda()
+    gs = torch.from_numpy(w["gauss"]).cuda() if w["gauss"].size else None
+    blocks, scales = api.harp_materialize_blocks(sch, d, th, gs, args.blk)
+    sg = torch.from_numpy(w["signs"]).cuda()
+    xall = torch.from_numpy(w["x"]).to(tdt).cuda()
+    ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
+    steps = max(args.steps, 20)
+    table = []
+    worst = 0.0
+    stream = torch.cuda.Stream()
+    for r in LAT_ROWS:
+        x = xall[:r].contiguous()
+        y = torch.empty_like(x)
+        with torch.cuda.stream(stream):
+            for _ in range(max(args.warmup, 5)):
+                api.harp_apply(sch, d, blocks, scales, sg, x, y, stream=stream)
+            stream.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(steps):
+                api.harp_apply(sch, d, blocks, scales, sg, x, y, stream=stream)
+            e1.record(stream)
+            host_s = time.perf_counter() - t0
+            stream.synchronize()
+            eager_us = e0.elapsed_time(e1) * 1e3 / steps
+            y_eager = y.clone()
+            y.zero_()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(steps):
+                    api.harp_apply(sch, d, blocks, scales, sg, x, y, stream=torch.cuda.current_stream())
+            stream.synchronize()
+            g.replay()
+            stream.synchronize()
+            e0.record(stream)
+            reps = 5
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            stream.synchronize()
+            graph_us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
+        if not torch.equal(y, y_eager):
+            print(f"graph replay output differs from the eager output at rows={r}", file=sys.stderr)
+            return 1
+        ref = O.apply(w["x"][:r].astype(np.float64), sch, ob, w["signs"].astype(float))
+        worst = max(worst, float(O.row_rel_l2(y.float().cpu().numpy(), ref).max()))
+        table.append({"rows": r, "us_per_call_eager": round(eager_us, 3),
+                      "us_per_call_host": round(host_s * 1e6 / steps, 3),
+                      "us_per_call_graph": round(graph_us, 3)})
+        del g
+    cbytes = sum(d * b for b in sch) * {"f32": 4, "bf16": 2, "i8": 1}[args.blk]
+    line = {
+        "metric": "HARP apply decode latency, microseconds per call (graph replay), rows=1",
+        "value": table[0]["us_per_call_graph"],
+        "unit": "us/call",
+        "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded rows and parameters of the named workload, first 1-64 rows)",
+        "config": {"workload": name, "d": d, "schedule": list(sch), "io": io, "blocks": args.blk,
+                   "kind": "apply-latency", "parallelism": "single GPU"},
+        "coefficient_bytes_per_call": cbytes,
+        "rows_table": table,
+        "parity_max_row_rel_l2": worst,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def materialize_main(args) -> int:
+    """Block materialisation and int8 parameter quantisation, microseconds per call."""
+    import torch
+
+    from oracle import harp_oracle as O
+    from structured_rotations_amd import api
+    from structured_rotations_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    w = W.make(name, rows=1)
+    if w["workload"].kind == "two_sided":
+        sides = [("u", w["su"], w["d_out"], w["theta_u"], w["gauss_u"]),
+                 ("v", w["schedule"], w["d"], w["theta_v"], w["gauss_v"])]
+    elif w["workload"].kind == "apply":
+        sides = [("", w["schedule"], w["d"], w["theta"], w["gauss"])]
+    else:
+        print("--mode materialize needs a workload with learnable blocks", file=sys.stderr)
+        return 2
+    steps = max(args.steps, 10)
+    out = []
+    for side, sch, d, theta, gauss in sides:
+        th = torch.from_numpy(theta).cuda()
+        gs = torch.from_numpy(gauss).cuda() if np.size(gauss) else None
+        codes, tsc = api.harp_quantize_theta(sch, d, th)
+        blk_out = torch.empty(api.harp_block_count(sch, d), dtype=torch.float32, device="cuda")
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return round(e0.elapsed_time(e1) * 1e3 / steps, 3)
+
+        t_q = timed(lambda: api.harp_quantize_theta(sch, d, th, codes, tsc))
+        t_f = timed(lambda: api.harp_materialize_blocks(sch, d, th, gs, "f32", blk_out))
+        t_8 = timed(lambda: api.harp_materialize_blocks_q8(sch, d, codes, tsc, gs, "f32", blk_out))
+        torch.cuda.synchronize()
+        c_ref, s_ref = O.quantize_theta(sch, d, theta)
+        ok = bool(np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(tsc.cpu().numpy(), s_ref))
+        ex = np.concatenate([b.ravel() for b in O.materialize_blocks(sch, d, O.dequantize_theta(sch, d, c_ref, s_ref),
+                                                                      gauss)])
+        got = blk_out.cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(got - ex) / (np.abs(ex) + 1e-30) * (np.abs(ex) > 1e-12)))
+        out.append({"side": side or "rows", "schedule": list(sch), "d": d,
+                    "n_theta": int(th.numel()), "n_scales": int(tsc.numel()),
+                    "us_quantize_theta": t_q, "us_materialize_f64_theta": t_f, "us_materialize_i8_theta": t_8,
+                    "codes_bit_exact": ok, "max_rel_err_blocks_f32": err})
+    line = {
+        "metric": "HARP block materialisation from int8 parameters, microseconds per call",
+        "value": round(sum(o["us_materialize_i8_theta"] for o in out), 3),
+        "unit": "us/call",
+        "n_gpus": 1, "steps": steps, "warmup": 3,
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (seeded parameters of the named workload)",
+        "config": {"workload": name, "kind": "materialize", "parallelism": "single GPU"},
+        "sides": out,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,11 +280,16 @@ def main() -> int:
                     help="time a plain device copy of the batch instead (counter calibration)")
     ap.add_argument("--flush", action="store_true",
                     help="per-launch timing with L2 and MALL flushed (a 1 GiB write) before every launch")
+    ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the apply path has no cross-GPU step and this build runs on a "
               "single MI355X; run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.mode == "latency":
+        return latency_main(args)
+    if args.mode == "materialize":
+        return materialize_main(args)
 
     import torch
 

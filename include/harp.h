@@ -125,6 +125,35 @@ harp_status harp_materialize_blocks(const harp_schedule* s, int64_t d,
                                     float* scales_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * int8 parameter storage   [TS §2.4: the learnable parameters may be kept in
+ * int8 with little loss]
+ *
+ * Codes: harp_theta_count() int8 values, in theta's layout.  Scales: one fp32
+ * per stage (s->m values), shared by all of that stage's parameters.  The
+ * value of a parameter is code * scale.  (A scale per stage, not per group,
+ * is what keeps the [TS §4] overhead of 2.00 -> 2.05 bits per weight.)
+ *
+ * harp_quantize_theta: scale = fp32(max|theta of the stage| / 127), code =
+ *   clamp(rint(theta / scale), -127, 127), decided in fp64; a stage of zeros
+ *   gets scale 0 and codes 0.  theta, theta_codes and theta_scales are device
+ *   pointers; the caller owns all three.
+ * harp_materialize_blocks_q8: as harp_materialize_blocks, with each parameter
+ *   formed on the device as the exact fp64 product code * scale; gauss,
+ *   blocks_out and scales_out as there.
+ * Both return HARP_ERR_INVALID_ARG (nothing launched) for a NULL pointer
+ * that is required or a schedule that does not factor d.
+ * ---------------------------------------------------------------------- */
+harp_status harp_quantize_theta(const harp_schedule* s, int64_t d,
+                                const double* theta, int8_t* theta_codes,
+                                float* theta_scales, hipStream_t stream);
+harp_status harp_materialize_blocks_q8(const harp_schedule* s, int64_t d,
+                                       const int8_t* theta_codes,
+                                       const float* theta_scales,
+                                       const double* gauss,
+                                       harp_dtype block_dtype, void* blocks_out,
+                                       float* scales_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Forward apply   y = S_{m-1} ... S_0 D_s x    for each of `rows` rows
  * [TS §2.1, §2.2; the deployment-time stride stages of TS §2.4].
  *

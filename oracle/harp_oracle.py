@@ -36,6 +36,8 @@ Readings of points the pages leave open:
       upper triangle filled row-major from the group's parameters.
   R9  Givens rotation [[cos t, -sin t], [sin t, cos t]].
   R10 one parameter set per (stage, group).
+  R11 int8 parameter storage: one fp32 scale per stage, symmetric, round to
+      nearest even, codes in [-127, 127].
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ import numpy as np
 __all__ = [
     "is_pow2", "sylvester", "qr_fallback", "mgs_qr", "givens", "cayley",
     "theta_counts", "gauss_stage_list", "materialize_blocks", "stage_strides",
+    "theta_groups", "quantize_theta", "dequantize_theta",
     "apply", "apply_inverse", "dense_operator", "fwht", "rht_compose",
     "rotate_weight", "round_bf16", "round_f32", "quantize_i8", "stored_blocks",
     "row_rel_l2", "unpack_bf16",
@@ -188,6 +191,57 @@ def materialize_blocks(schedule, d: int, theta: np.ndarray, gauss: np.ndarray | 
     if gpos != gauss.size:
         raise ValueError("gauss has the wrong length")
     return blocks
+
+
+def theta_groups(schedule, d: int) -> list[tuple[int, int]]:
+    """(number of groups, parameters per group) for every stage: one angle per
+    group for radix 2, b(b-1)/2 skew entries per group otherwise."""
+    return [(d // b, 1 if b == 2 else b * (b - 1) // 2) for b in schedule]
+
+
+def quantize_theta(schedule, d: int, theta: np.ndarray):
+    """Symmetric int8 storage of the learnable parameters [TS §2.4: the
+    parameters may be kept in int8].  Reading R11: one fp32 scale per stage,
+    shared by all of that stage's parameters; scale = fp32(max|theta_stage| /
+    127), code = clip(rint(theta / scale), -127, 127) with the decision taken
+    in fp64; a stage of zeros gets scale 0 and codes 0.
+    Returns (codes int8 of theta's length, scales fp32, one per stage)."""
+    _check_schedule(schedule, d)
+    theta = np.asarray(theta, dtype=np.float64).ravel()
+    codes, scales = [], []
+    pos = 0
+    for ng, per in theta_groups(schedule, d):
+        th = theta[pos:pos + ng * per]
+        pos += ng * per
+        amax = np.abs(th).max() if th.size else 0.0
+        scale = float(np.float32(amax / 127.0))
+        if scale > 0:
+            code = np.clip(np.rint(th / scale), -127, 127)
+        else:
+            code = np.zeros_like(th)
+        codes.append(code.astype(np.int8))
+        scales.append(scale)
+    if pos != theta.size:
+        raise ValueError("theta has the wrong length")
+    return np.concatenate(codes), np.array(scales, dtype=np.float32)
+
+
+def dequantize_theta(schedule, d: int, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """theta = code * scale for every parameter, with its stage's scale
+    (reading R11).  The product of an int8 and an fp32 is exact in fp64."""
+    _check_schedule(schedule, d)
+    codes = np.asarray(codes).ravel().astype(np.float64)
+    scales = np.asarray(scales, dtype=np.float32).ravel().astype(np.float64)
+    if scales.size != len(schedule):
+        raise ValueError("one scale per stage expected")
+    out = []
+    pos = 0
+    for t, (ng, per) in enumerate(theta_groups(schedule, d)):
+        out.append(codes[pos:pos + ng * per] * scales[t])
+        pos += ng * per
+    if pos != codes.size:
+        raise ValueError("codes have the wrong length")
+    return np.concatenate(out)
 
 
 # --------------------------------------------------------------------------

@@ -53,6 +53,8 @@ _SIG = {
     "harp_block_count": (_I64, [ctypes.POINTER(Schedule), _I64]),
     "harp_group_count": (_I64, [ctypes.POINTER(Schedule), _I64]),
     "harp_materialize_blocks": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _P, _I32, _P, _P, _P]),
+    "harp_quantize_theta": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _P, _P, _P]),
+    "harp_materialize_blocks_q8": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _P, _P, _I32, _P, _P, _P]),
     "harp_apply": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64, _I64, _I32, _P]),
     "harp_apply_inverse": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64, _I64,
                                   _I32, _P]),

@@ -88,6 +88,56 @@ def harp_materialize_blocks(schedule, d: int, theta: torch.Tensor, gauss: torch.
     return blocks_out, (scales_out if block_dtype == "i8" else None)
 
 
+def harp_quantize_theta(schedule, d: int, theta: torch.Tensor, codes_out: torch.Tensor | None = None,
+                        scales_out: torch.Tensor | None = None, stream=None):
+    """int8 codes and one fp32 scale per stage of fp64 theta, on device.
+    Returns (codes, scales)."""
+    _dev(theta, "theta")
+    if theta.dtype != torch.float64 or not theta.is_contiguous():
+        raise TypeError("theta must be contiguous float64")
+    if codes_out is None:
+        codes_out = torch.empty(harp_theta_count(schedule, d), dtype=torch.int8, device=theta.device)
+    if scales_out is None:
+        scales_out = torch.empty(len(tuple(schedule)), dtype=torch.float32, device=theta.device)
+    _dev(codes_out, "codes_out")
+    _dev(scales_out, "scales_out")
+    check(lib().harp_quantize_theta(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta), _ptr(codes_out),
+                                    _ptr(scales_out), _stream(stream)))
+    return codes_out, scales_out
+
+
+def harp_materialize_blocks_q8(schedule, d: int, theta_codes: torch.Tensor, theta_scales: torch.Tensor,
+                               gauss: torch.Tensor | None, block_dtype: str = "f32",
+                               blocks_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                               stream=None):
+    """As harp_materialize_blocks, with theta given as int8 codes and one fp32
+    scale per stage.  Returns (blocks, scales|None)."""
+    _dev(theta_codes, "theta_codes")
+    _dev(theta_scales, "theta_scales")
+    _dev(gauss, "gauss")
+    if theta_codes.dtype != torch.int8 or theta_scales.dtype != torch.float32:
+        raise TypeError("theta_codes must be int8 and theta_scales float32")
+    if gauss is not None and gauss.dtype != torch.float64:
+        raise TypeError("gauss must be float64")
+    if not theta_codes.is_contiguous() or not theta_scales.is_contiguous() or \
+            (gauss is not None and not gauss.is_contiguous()):
+        raise ValueError("theta_codes, theta_scales and gauss must be contiguous")
+    if theta_codes.numel() != harp_theta_count(schedule, d) or \
+            theta_scales.numel() != len(tuple(schedule)):
+        raise ValueError("theta_codes / theta_scales have the wrong length for this schedule")
+    tdt = _BLK_NAME[block_dtype]
+    if blocks_out is None:
+        blocks_out = torch.empty(harp_block_count(schedule, d), dtype=tdt, device=theta_codes.device)
+    if block_dtype == "i8" and scales_out is None:
+        scales_out = torch.empty(harp_group_count(schedule, d), dtype=torch.float32, device=theta_codes.device)
+    _dev(blocks_out, "blocks_out")
+    _dev(scales_out, "scales_out")
+    check(lib().harp_materialize_blocks_q8(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta_codes),
+                                           _ptr(theta_scales), _ptr(gauss), _DT[tdt], _ptr(blocks_out),
+                                           _ptr(scales_out), _stream(stream)))
+    return blocks_out, (scales_out if block_dtype == "i8" else None)
+
+
 # ------------------------------------------------------------------ apply
 def _apply(fn, schedule, d, blocks, scales, signs, x, y, stream):
     _dev(blocks, "blocks")

@@ -99,9 +99,40 @@ harp_status harp_materialize_blocks(const harp_schedule* s, int64_t d, const dou
   if (blocks_out == nullptr) return fail(HARP_ERR_INVALID_ARG, "blocks_out is NULL");
   if ((block_dtype == HARP_I8) != (scales_out != nullptr))
     return fail(HARP_ERR_INVALID_ARG, "scales_out must be given exactly for HARP_I8 blocks");
-  return launch_status(harp::launch_materialize(pl, theta, gauss, static_cast<DT>(block_dtype), blocks_out,
-                                                scales_out, stream),
+  return launch_status(harp::launch_materialize(pl, theta, nullptr, nullptr, gauss, static_cast<DT>(block_dtype),
+                                                blocks_out, scales_out, stream),
                        "harp_materialize_blocks");
+}
+
+harp_status harp_quantize_theta(const harp_schedule* s, int64_t d, const double* theta, int8_t* theta_codes,
+                                float* theta_scales, hipStream_t stream) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err)) return fail(HARP_ERR_INVALID_ARG, err);
+  if (theta == nullptr) return fail(HARP_ERR_INVALID_ARG, "theta is NULL");
+  if (theta_codes == nullptr) return fail(HARP_ERR_INVALID_ARG, "theta_codes is NULL");
+  if (theta_scales == nullptr) return fail(HARP_ERR_INVALID_ARG, "theta_scales is NULL");
+  return launch_status(harp::launch_quantize_theta(pl, theta, theta_codes, theta_scales, stream),
+                       "harp_quantize_theta");
+}
+
+harp_status harp_materialize_blocks_q8(const harp_schedule* s, int64_t d, const int8_t* theta_codes,
+                                       const float* theta_scales, const double* gauss, harp_dtype block_dtype,
+                                       void* blocks_out, float* scales_out, hipStream_t stream) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err)) return fail(HARP_ERR_INVALID_ARG, err);
+  if (!blk_ok(block_dtype)) return fail(HARP_ERR_UNSUPPORTED, "block_dtype must be HARP_F32, HARP_BF16 or HARP_I8");
+  if (theta_codes == nullptr) return fail(HARP_ERR_INVALID_ARG, "theta_codes is NULL");
+  if (theta_scales == nullptr) return fail(HARP_ERR_INVALID_ARG, "theta_scales is NULL");
+  if (pl.n_gauss > 0 && gauss == nullptr)
+    return fail(HARP_ERR_INVALID_ARG, "gauss is NULL but the schedule has a non-power-of-two radix");
+  if (blocks_out == nullptr) return fail(HARP_ERR_INVALID_ARG, "blocks_out is NULL");
+  if ((block_dtype == HARP_I8) != (scales_out != nullptr))
+    return fail(HARP_ERR_INVALID_ARG, "scales_out must be given exactly for HARP_I8 blocks");
+  return launch_status(harp::launch_materialize(pl, nullptr, theta_codes, theta_scales, gauss,
+                                                static_cast<DT>(block_dtype), blocks_out, scales_out, stream),
+                       "harp_materialize_blocks_q8");
 }
 
 harp_status harp_apply(const harp_schedule* s, int64_t d, const void* blocks, harp_dtype block_dtype,

@@ -55,7 +55,13 @@ hipError_t launch_rht(const Plan& pl, const int8_t* signs, int k, bool inverse, 
                       hipStream_t stream);
 
 // B_{t,c} = Q_{t,c}(theta) G_{b_t} for all stages, in fp64, rounded to bdt.
-hipError_t launch_materialize(const Plan& pl, const double* theta, const double* gauss, DT bdt,
-                              void* blocks, float* scales, hipStream_t stream);
+// theta is fp64, or (theta NULL) int8 codes tcode with one fp32 scale per stage.
+hipError_t launch_materialize(const Plan& pl, const double* theta, const int8_t* tcode,
+                              const float* tscale, const double* gauss, DT bdt, void* blocks,
+                              float* scales, hipStream_t stream);
+
+// int8 codes + one fp32 scale per stage of fp64 theta.
+hipError_t launch_quantize_theta(const Plan& pl, const double* theta, int8_t* codes, float* scales,
+                                 hipStream_t stream);
 
 }  // namespace harp

@@ -6,7 +6,10 @@
 // Sylvester Hadamard for power-of-two radices, otherwise the Q factor of the
 // QR factorisation of a fixed Gaussian matrix, §2.1).  With all parameters
 // zero, Q = I and the block is G.  §2.4: parameters may be stored in int8;
-// the same idea is offered here for the blocks (one fp32 scale per block).
+// the same idea is offered here for the blocks (one fp32 scale per block),
+// and the parameters themselves may come in as int8 codes with one fp32 scale
+// per stage: theta = code * scale, formed exactly in fp64 before the same
+// solve.  quantize_theta_kernel produces that format from fp64 theta.
 //
 // One launch per stage.  Thread 0 of each workgroup builds G in LDS
 // (Householder QR with the column signs fixed so that diag R > 0); every
@@ -22,7 +25,9 @@ namespace harp {
 
 struct MatParams {
   int64_t ngroups;
-  const double* theta;   // the stage's parameters
+  const double* theta;   // the stage's parameters (fp64), or NULL when tcode is given
+  const int8_t* tcode;   // the stage's int8 parameter codes, or NULL
+  const float* tscale;   // the stage's fp32 scale (with tcode)
   const double* gauss;   // the stage's b x b Gaussian matrix, or NULL
   int out_dt;            // 0 F32, 1 BF16, 2 I8
   void* out;             // the stage's blocks
@@ -75,6 +80,12 @@ __device__ void base_mixer(const double* gauss, double* g) {
   }
 }
 
+// Parameter i of group c (per parameters per group), dequantised if int8.
+__device__ inline double param(const MatParams& p, int64_t c, int per, int i) {
+  if (p.tcode != nullptr) return (double)p.tcode[c * per + i] * (double)p.tscale[0];
+  return p.theta[c * per + i];
+}
+
 template <int B>
 __global__ void __launch_bounds__(256) materialize_kernel(MatParams p) {
   __shared__ double g[B * B];
@@ -84,20 +95,19 @@ __global__ void __launch_bounds__(256) materialize_kernel(MatParams p) {
   if (c >= p.ngroups) return;
   double q[B][B];
   if (B == 2) {
-    const double th = p.theta[c];
+    const double th = param(p, c, 1, 0);
     const double cs = cos(th), sn = sin(th);
     q[0][0] = cs; q[0][1] = -sn;
     q[1][0] = sn; q[1][1] = cs;
   } else {
     constexpr int per = B * (B - 1) / 2;
-    const double* th = p.theta + c * per;
     double mtx[B][B];
     for (int r = 0; r < B; ++r)
       for (int k = 0; k < B; ++k) { mtx[r][k] = (r == k) ? 1.0 : 0.0; q[r][k] = mtx[r][k]; }
     int idx = 0;
     for (int r = 0; r < B; ++r)
       for (int k = r + 1; k < B; ++k) {
-        const double a = th[idx++];
+        const double a = param(p, c, per, idx++);
         mtx[r][k] += a; mtx[k][r] -= a;   // I + A
         q[r][k] -= a;   q[k][r] += a;     // I - A
       }
@@ -149,6 +159,28 @@ __global__ void __launch_bounds__(256) materialize_kernel(MatParams p) {
   }
 }
 
+// One workgroup per stage: scale = fp32(max|theta of the stage| / 127), code =
+// clamp(rint(theta / scale), -127, 127) decided in fp64; a zero stage -> 0, 0.
+constexpr int kQThreads = 1024;
+__global__ void __launch_bounds__(kQThreads) quantize_theta_kernel(int64_t n, const double* theta, int8_t* codes,
+                                                                   float* scale_out) {
+  __shared__ double red[kQThreads / 64];
+  double amax = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += kQThreads) amax = fmax(amax, fabs(theta[i]));
+  for (int off = 32; off > 0; off >>= 1) amax = fmax(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+  for (int w = 1; w < kQThreads / 64; ++w) amax = fmax(amax, red[w]);
+  const float sc = (float)(amax / 127.0);
+  if (threadIdx.x == 0) scale_out[0] = sc;
+  for (int64_t i = threadIdx.x; i < n; i += kQThreads) {
+    double code = 0.0;
+    if (sc > 0.0f) code = fmin(127.0, fmax(-127.0, rint(theta[i] / (double)sc)));
+    codes[i] = (int8_t)code;
+  }
+}
+
 namespace {
 template <int B>
 hipError_t launch_mat(const MatParams& p, hipStream_t st) {
@@ -159,13 +191,16 @@ hipError_t launch_mat(const MatParams& p, hipStream_t st) {
 }
 }  // namespace
 
-hipError_t launch_materialize(const Plan& pl, const double* theta, const double* gauss, DT bdt,
-                              void* blocks, float* scales, hipStream_t stream) {
+hipError_t launch_materialize(const Plan& pl, const double* theta, const int8_t* tcode,
+                              const float* tscale, const double* gauss, DT bdt, void* blocks,
+                              float* scales, hipStream_t stream) {
   const int esz = bdt == DT::F32 ? 4 : (bdt == DT::BF16 ? 2 : 1);
   for (int t = 0; t < pl.m; ++t) {
     MatParams p{};
     p.ngroups = pl.d / pl.radix[t];
-    p.theta = theta + pl.theta_off[t];
+    p.theta = theta ? theta + pl.theta_off[t] : nullptr;
+    p.tcode = tcode ? tcode + pl.theta_off[t] : nullptr;
+    p.tscale = tscale ? tscale + t : nullptr;
     p.gauss = pl.gauss_off[t] >= 0 ? gauss + pl.gauss_off[t] : nullptr;
     p.out_dt = (int)bdt;
     p.out = static_cast<char*>(blocks) + pl.blk_off[t] * esz;
@@ -189,6 +224,19 @@ hipError_t launch_materialize(const Plan& pl, const double* theta, const double*
       case 16: e = launch_mat<16>(p, stream); break;
       default: e = hipErrorInvalidValue; break;
     }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_quantize_theta(const Plan& pl, const double* theta, int8_t* codes, float* scales,
+                                 hipStream_t stream) {
+  for (int t = 0; t < pl.m; ++t) {
+    const int b = pl.radix[t];
+    const int64_t n = (pl.d / b) * (b == 2 ? 1 : b * (b - 1) / 2);
+    hipLaunchKernelGGL(quantize_theta_kernel, dim3(1), dim3(kQThreads), 0, stream, n, theta + pl.theta_off[t],
+                       codes + pl.theta_off[t], scales + t);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

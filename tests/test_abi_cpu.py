@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_abi():
     names = _declared_functions()
     for want in ("harp_apply", "harp_apply_inverse", "harp_rotate_weight", "rht_compose",
-                 "harp_materialize_blocks", "harp_status_str", "harp_last_error"):
+                 "harp_materialize_blocks", "harp_quantize_theta", "harp_materialize_blocks_q8",
+                 "harp_status_str", "harp_last_error"):
         assert want in names
 
 
@@ -123,6 +124,22 @@ def test_materialize_rejects_on_host(lib):
     assert lib.harp_materialize_blocks(s, 40, None, FAKE, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
     assert lib.harp_materialize_blocks(s, 40, FAKE, FAKE, 2, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
     assert lib.harp_materialize_blocks(s, 40, FAKE, FAKE, 3, FAKE2, None, None) == _lib.HARP_ERR_UNSUPPORTED
+
+
+def test_theta_i8_entry_points_reject_on_host(lib):
+    s = ctypes.byref(Schedule.of((8, 5)))
+    q8 = lib.harp_materialize_blocks_q8
+    assert q8(s, 40, None, FAKE, FAKE, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert q8(s, 40, FAKE, None, FAKE, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert q8(s, 40, FAKE, FAKE, None, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert q8(s, 40, FAKE, FAKE, FAKE, 2, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert q8(s, 40, FAKE, FAKE, FAKE, 3, FAKE2, None, None) == _lib.HARP_ERR_UNSUPPORTED
+    assert q8(s, 41, FAKE, FAKE, FAKE, 0, FAKE2, None, None) == _lib.HARP_ERR_INVALID_ARG
+    qt = lib.harp_quantize_theta
+    assert qt(s, 40, None, FAKE, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
+    assert qt(s, 40, FAKE, None, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
+    assert qt(s, 40, FAKE, FAKE, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert qt(s, 41, FAKE, FAKE, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
 
 
 def test_rotate_weight_rejects_on_host(lib):

@@ -67,6 +67,62 @@ def test_materialize_matches_oracle(name, side, blk):
     assert np.mean(got != ref) < 1e-4
 
 
+# ------------------------------------------------------------------ int8 parameters
+@pytest.mark.parametrize("name,side", MAT_CASES)
+def test_quantize_theta_matches_oracle(name, side):
+    # Integer codes: bit-exact.  Both sides divide and round in fp64.
+    sch, d, theta, _ = _mat_inputs(name, side)
+    codes_ref, scales_ref = O.quantize_theta(sch, d, theta)
+    codes, scales = api.harp_quantize_theta(sch, d, torch.from_numpy(np.ascontiguousarray(theta)).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales.cpu().numpy(), scales_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
+
+
+@pytest.mark.parametrize("name,side", MAT_CASES)
+@pytest.mark.parametrize("blk", ["f32", "bf16", "i8"])
+def test_materialize_q8_matches_oracle(name, side, blk):
+    # Blocks from int8 parameters against the oracle's blocks from the same
+    # dequantised parameters (code * scale is exact in fp64 on both sides).
+    sch, d, theta, gauss = _mat_inputs(name, side)
+    codes, scales = O.quantize_theta(sch, d, theta)
+    exact = O.materialize_blocks(sch, d, O.dequantize_theta(sch, d, codes, scales), gauss)
+    ex = np.concatenate([b.ravel() for b in exact])
+    gs = torch.from_numpy(np.ascontiguousarray(gauss, dtype=np.float64)).cuda() \
+        if gauss is not None and np.size(gauss) else None
+    blocks, bsc = api.harp_materialize_blocks_q8(sch, d, torch.from_numpy(codes).cuda(),
+                                                 torch.from_numpy(scales).cuda(), gs, blk)
+    torch.cuda.synchronize()
+    if blk == "i8":
+        codes_ref, scales_ref = zip(*[O.quantize_i8(b) for b in exact])
+        codes_ref = np.concatenate([c.ravel() for c in codes_ref]).astype(np.int64)
+        scales_ref = np.concatenate(scales_ref).astype(np.float64)
+        np.testing.assert_allclose(bsc.cpu().numpy().astype(np.float64), scales_ref, rtol=2.0 ** -23, atol=0)
+        per = np.repeat(scales_ref, [b * b for b in sch for _ in range(d // b)])
+        frac = np.abs(ex / per - np.floor(ex / per) - 0.5)
+        got = blocks.cpu().numpy().astype(np.int64)
+        assert np.all((got == codes_ref) | (frac < 1e-6))
+        return
+    got = from_dev(blocks)
+    ulp = 2.0 ** -24 if blk == "f32" else 2.0 ** -8
+    assert np.all(np.abs(got - ex) <= ulp * np.abs(ex) + 1e-14)
+
+
+def test_materialize_q8_equals_fp64_entry_on_dequantised_theta():
+    # The int8 entry point and the fp64 entry point given code * scale
+    # produce the same bytes (same kernel arithmetic after dequantisation).
+    w = _case("mixed5120_bf16", rows=1)
+    sch, d = w["schedule"], w["d"]
+    codes, scales = O.quantize_theta(sch, d, w["theta"])
+    th = torch.from_numpy(O.dequantize_theta(sch, d, codes, scales)).cuda()
+    gs = torch.from_numpy(np.ascontiguousarray(w["gauss"])).cuda()
+    a, _ = api.harp_materialize_blocks(sch, d, th, gs, "f32")
+    b, _ = api.harp_materialize_blocks_q8(sch, d, torch.from_numpy(codes).cuda(),
+                                          torch.from_numpy(scales).cuda(), gs, "f32")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ apply / inverse
 APPLY = ["sylvester64_f32", "cayley4096_bf16", "mixed5120_bf16"]
 SMALL_ROWS = {"sylvester64_f32": 256, "cayley4096_bf16": 37, "mixed5120_bf16": 29}

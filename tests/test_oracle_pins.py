@@ -415,3 +415,84 @@ def test_golden_small_cases_regression():
         blocks = O.materialize_blocks(sch, d, np.array(case["theta"]), np.array(case["gauss"]))
         y = O.apply(np.array(case["x"]), sch, blocks, np.array(case["signs"], dtype=float))
         np.testing.assert_allclose(y, np.array(case["y"]), atol=1e-14)
+
+
+# ------------------------------------------------------------------ int8 parameter storage
+def test_theta_i8_hand_example():
+    # [TS §2.4] parameters may be stored in int8; the per-stage scale is
+    # reading R11.  The fixture was worked out by hand: a per-group scale, a
+    # wrong stage split or a dropped rounding all give other codes.
+    with open(os.path.join(GOLDEN, "theta_i8_hand.json")) as f:
+        case = json.load(f)
+    sch, d = tuple(case["schedule"]), case["d"]
+    codes, scales = O.quantize_theta(sch, d, np.array(case["theta"]))
+    assert codes.dtype == np.int8 and scales.dtype == np.float32
+    np.testing.assert_array_equal(codes.astype(int), case["codes"])
+    want = np.array([np.float32(n / q) for n, q in case["scale_quotients"]], dtype=np.float32)
+    np.testing.assert_array_equal(scales, want)
+    back = O.dequantize_theta(sch, d, codes, scales)
+    np.testing.assert_array_equal(back, np.array(case["codes"], dtype=float) *
+                                  np.repeat(want.astype(float), [6, 12, 6]))
+
+
+def test_theta_i8_scale_granularity_matches_bits_per_param():
+    # [TS §4] int8 HARP parameters raise bits per parameter from 2.00 to 2.05
+    # (2-bit model).  On a two-sided (8,8,8,8) processor of a 4096 x 4096
+    # layer, per-stage fp32 scales keep that figure; per-group fp32 scales
+    # would add 0.008 bits and give 2.06 (reading R11).
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        bpp = json.load(f)["bits_per_param"]
+    d, sch = 4096, (8, 8, 8, 8)
+    codes_bits = 2 * sum(O.theta_counts(sch, d)) * 8
+    per_stage = codes_bits + 2 * len(sch) * 32
+    per_group = codes_bits + 2 * sum(d // b for b in sch) * 32
+    assert round(bpp["base"] + per_stage / d ** 2, 2) == bpp["with_harp_int8"]
+    assert round(bpp["base"] + per_group / d ** 2, 2) != bpp["with_harp_int8"]
+
+
+@pytest.mark.parametrize("sch,d", [((8, 8), 64), ((2, 5, 4), 40), ((16, 2, 3), 96)])
+def test_theta_i8_properties(sch, d):
+    # Symmetric rounding to the nearest code: the error per parameter is at
+    # most half its stage's scale, each stage's largest magnitude maps to
+    # +-127, negation commutes with quantisation, and dequantisation returns
+    # the exact product code * scale.
+    n = sum(O.theta_counts(sch, d))
+    theta = RNG.standard_normal(n) * 0.3
+    codes, scales = O.quantize_theta(sch, d, theta)
+    assert codes.size == n and scales.size == len(sch)
+    back = O.dequantize_theta(sch, d, codes, scales)
+    counts = O.theta_counts(sch, d)
+    sscale = np.repeat(scales.astype(np.float64), counts)
+    assert np.all(np.abs(back - theta) <= 0.5 * sscale * (1 + 1e-12))
+    lo = 0
+    for n_t in counts:
+        assert np.abs(codes[lo:lo + n_t].astype(int)).max() == 127
+        lo += n_t
+    nc, ns = O.quantize_theta(sch, d, -theta)
+    np.testing.assert_array_equal(nc, -codes)
+    np.testing.assert_array_equal(ns, scales)
+    np.testing.assert_array_equal(back, codes.astype(np.float64) * sscale)
+
+
+def test_theta_i8_zero_and_cayley_lipschitz():
+    # All-zero parameters quantise to zero codes and scales, so the blocks are
+    # the base mixers G [TS §2.2].  For skew A, ||(I + A)^-1||_2 <= 1, so the
+    # Cayley factor moves by at most 2 ||dA||_2 + O(dA^2) when the parameters
+    # are rounded to int8.
+    sch, d = (8, 4), 32
+    n = sum(O.theta_counts(sch, d))
+    codes, scales = O.quantize_theta(sch, d, np.zeros(n))
+    assert not codes.any() and not scales.any()
+    theta = RNG.standard_normal(n) * 0.2
+    codes, scales = O.quantize_theta(sch, d, theta)
+    back = O.dequantize_theta(sch, d, codes, scales)
+    b0 = O.materialize_blocks(sch, d, theta, None)
+    b1 = O.materialize_blocks(sch, d, back, None)
+    pos = 0
+    for t, b in enumerate(sch):
+        per = b * (b - 1) // 2
+        for c in range(d // b):
+            da = O.skew_from_params(back[pos:pos + per], b) - O.skew_from_params(theta[pos:pos + per], b)
+            pos += per
+            bound = 2 * np.linalg.norm(da, 2)
+            assert np.linalg.norm(b1[t][c] - b0[t][c], 2) <= bound * 1.05 + 1e-15
