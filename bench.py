@@ -16,12 +16,12 @@ device synchronisation).  roofline.achieved = algorithmic bytes per launch
 duration, measured with HIP events recorded on the stream the kernel runs on.
 cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
 
---mode latency: the per-token (decode) regime, 1 to 64 rows per call.  For
-each row count: microseconds per call of K back-to-back calls issued from
-Python (host launch cost included), and of the same calls captured once in a
-HIP graph and replayed (device time per call, launch gaps included), with the
-output of the graph replay checked against eager calls and, for some rows,
-against the oracle.
+--mode latency: the per-token (decode) regime, 1 to 64 rows per call, for
+harp_apply_decode and, beside it, harp_apply.  For each row count:
+microseconds per call of K back-to-back calls issued from Python (host launch
+cost included), and of the same calls captured once in a HIP graph and
+replayed (device time per call, launch gaps included); the replay's output is
+checked against the eager calls and both entry points against the oracle.
 
 --mode materialize: microseconds per call of the block materialisation on the
 device from fp64 parameters and from int8 parameter codes, and of the int8
@@ -113,7 +113,8 @@ LAT_ROWS = (1, 2, 4, 8, 16, 32, 64)
 
 
 def latency_main(args) -> int:
-    """Decode regime: microseconds per harp_apply call at 1-64 rows."""
+    """Decode regime: microseconds per call at 1-64 rows, for harp_apply_decode
+    (the small-batch entry point) and, beside it, harp_apply."""
     import torch
 
     from oracle import harp_oracle as O
@@ -133,23 +134,24 @@ def latency_main(args) -> int:
     blocks, scales = api.harp_materialize_blocks(sch, d, th, gs, args.blk)
     sg = torch.from_numpy(w["signs"]).cuda()
     xall = torch.from_numpy(w["x"]).to(tdt).cuda()
+    ws_bytes = api.harp_apply_decode_workspace(sch, d, args.blk, max(LAT_ROWS))
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
     ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
     steps = max(args.steps, 20)
-    table = []
-    worst = 0.0
+    warm = max(args.warmup, 5)
     stream = torch.cuda.Stream()
-    for r in LAT_ROWS:
-        x = xall[:r].contiguous()
-        y = torch.empty_like(x)
+
+    def measure(call, y):
+        """(eager us/call, host us/call, graph-replay us/call, output of the replay)."""
         with torch.cuda.stream(stream):
-            for _ in range(max(args.warmup, 5)):
-                api.harp_apply(sch, d, blocks, scales, sg, x, y, stream=stream)
+            for _ in range(warm):
+                call()
             stream.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             t0 = time.perf_counter()
             e0.record(stream)
             for _ in range(steps):
-                api.harp_apply(sch, d, blocks, scales, sg, x, y, stream=stream)
+                call()
             e1.record(stream)
             host_s = time.perf_counter() - t0
             stream.synchronize()
@@ -159,32 +161,44 @@ def latency_main(args) -> int:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for _ in range(steps):
-                    api.harp_apply(sch, d, blocks, scales, sg, x, y, stream=torch.cuda.current_stream())
+                    call()
             stream.synchronize()
             g.replay()
             stream.synchronize()
-            e0.record(stream)
             reps = 5
+            e0.record(stream)
             for _ in range(reps):
                 g.replay()
             e1.record(stream)
             stream.synchronize()
             graph_us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
+            del g
         if not torch.equal(y, y_eager):
-            print(f"graph replay output differs from the eager output at rows={r}", file=sys.stderr)
-            return 1
+            raise RuntimeError("graph replay output differs from the eager output")
+        return eager_us, host_s * 1e6 / steps, graph_us
+
+    table = []
+    worst = 0.0
+    for r in LAT_ROWS:
+        x = xall[:r].contiguous()
+        yd = torch.empty_like(x)
+        ya = torch.empty_like(x)
+        dec = measure(lambda: api.harp_apply_decode(sch, d, blocks, scales, sg, x, yd, workspace=ws,
+                                                    stream=stream), yd)
+        app = measure(lambda: api.harp_apply(sch, d, blocks, scales, sg, x, ya, stream=stream), ya)
         ref = O.apply(w["x"][:r].astype(np.float64), sch, ob, w["signs"].astype(float))
-        worst = max(worst, float(O.row_rel_l2(y.float().cpu().numpy(), ref).max()))
-        table.append({"rows": r, "us_per_call_eager": round(eager_us, 3),
-                      "us_per_call_host": round(host_s * 1e6 / steps, 3),
-                      "us_per_call_graph": round(graph_us, 3)})
-        del g
+        worst = max(worst, float(O.row_rel_l2(yd.float().cpu().numpy(), ref).max()),
+                    float(O.row_rel_l2(ya.float().cpu().numpy(), ref).max()))
+        table.append({"rows": r,
+                      "decode_us_graph": round(dec[2], 3), "decode_us_eager": round(dec[0], 3),
+                      "decode_us_host": round(dec[1], 3),
+                      "apply_us_graph": round(app[2], 3), "apply_us_eager": round(app[0], 3)})
     cbytes = sum(d * b for b in sch) * {"f32": 4, "bf16": 2, "i8": 1}[args.blk]
     line = {
         "metric": "HARP apply decode latency, microseconds per call (graph replay), rows=1",
-        "value": table[0]["us_per_call_graph"],
+        "value": table[0]["decode_us_graph"],
         "unit": "us/call",
-        "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 5),
+        "n_gpus": 1, "steps": steps, "warmup": warm,
         "higher_is_better": False,
         "vs_baseline": None,
         "dtype": "f32",

@@ -182,6 +182,37 @@ harp_status harp_apply_inverse(const harp_schedule* s, int64_t d,
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Small-batch (per-token decode) apply   [TS §2.1; TS §4 quotes the
+ * transform's cost per generated token]
+ *
+ *   inverse == 0:  y = S_{m-1} ... S_0 D_s x       (as harp_apply)
+ *   inverse != 0:  y = D_s S_0^T ... S_{m-1}^T x   (as harp_apply_inverse)
+ *
+ * For 1 <= rows <= HARP_DECODE_MAX_ROWS; built for latency at 1-64 rows.
+ * The digits are split into two runs and each run is one launch of many
+ * small workgroups; fp32 rows are handed from the first launch to the second
+ * through `workspace`, so the arithmetic is fp32 throughout as in harp_apply.
+ * harp_apply_decode_workspace() gives the bytes needed (rows * d * 4, or 0
+ * when the whole row fits one workgroup and a single launch is made), or -1
+ * if no split of the schedule fits (then harp_apply_decode returns
+ * HARP_ERR_UNSUPPORTED).  workspace: device memory owned by the caller,
+ * 4-byte aligned, not overlapping x or y; its contents are scratch.  Calls
+ * that share one workspace must not overlap in time.  x and y may be the same
+ * buffer (with ldx == ldy).  Other arguments, layouts and errors as
+ * harp_apply; rows == 0 returns HARP_OK without a launch.
+ * ---------------------------------------------------------------------- */
+#define HARP_DECODE_MAX_ROWS 1024
+int64_t harp_apply_decode_workspace(const harp_schedule* s, int64_t d,
+                                    harp_dtype block_dtype, int64_t rows);
+harp_status harp_apply_decode(const harp_schedule* s, int64_t d,
+                              const void* blocks, harp_dtype block_dtype,
+                              const float* block_scales, const int8_t* signs,
+                              const void* x, int64_t ldx, void* y, int64_t ldy,
+                              int64_t rows, harp_dtype io_dtype, int32_t inverse,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Two-sided weight rotation [TS §2, §3; ABS: a two-sided processor]
  *   inverse == 0:  W_out = M_U W M_V^T      (M_V on every row of W,
  *                                           M_U on every column)

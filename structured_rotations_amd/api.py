@@ -168,6 +168,43 @@ def harp_apply_inverse(schedule, d: int, blocks, scales, signs, y, x=None, strea
     return _apply(lib().harp_apply_inverse, schedule, d, blocks, scales, signs, y, x, stream)
 
 
+def harp_apply_decode_workspace(schedule, d: int, block_dtype: str, rows: int) -> int:
+    """Workspace bytes harp_apply_decode needs (0: one launch, -1: unsupported)."""
+    return int(lib().harp_apply_decode_workspace(ctypes.byref(Schedule.of(schedule)), d,
+                                                 _DT[_BLK_NAME[block_dtype]], rows))
+
+
+def harp_apply_decode(schedule, d: int, blocks, scales, signs, x, y=None, inverse: bool = False,
+                      workspace=None, stream=None):
+    """Small-batch apply (1 to a few hundred rows), forward or inverse.
+    workspace: a device tensor of at least harp_apply_decode_workspace() bytes
+    (allocated here when None and needed)."""
+    _dev(blocks, "blocks")
+    _dev(scales, "scales")
+    _dev(signs, "signs")
+    _dev(x, "x")
+    _dev(workspace, "workspace")
+    rows, ldx = _rows_ld(x, d, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y")
+    rows_y, ldy = _rows_ld(y, d, "y")
+    if rows_y != rows or y.dtype != x.dtype:
+        raise ValueError("y must match x in rows and dtype")
+    if signs is not None and signs.dtype != torch.int8:
+        raise TypeError("signs must be int8")
+    sch = Schedule.of(schedule)
+    if workspace is None:
+        need = int(lib().harp_apply_decode_workspace(ctypes.byref(sch), d, _DT[blocks.dtype], rows))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().harp_apply_decode(ctypes.byref(sch), d, _ptr(blocks), _DT[blocks.dtype], _ptr(scales),
+                                  _ptr(signs), _ptr(x), ldx, _ptr(y), ldy, rows, _DT[x.dtype], int(inverse),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
 def harp_rotate_weight(su, blocks_u, scales_u, signs_u, sv, blocks_v, scales_v, signs_v, w,
                        w_out=None, inverse: bool = False, workspace=None, stream=None):
     """W_out = M_U W M_V^T (inverse: M_U^T W M_V); W is prod(su) x prod(sv)."""

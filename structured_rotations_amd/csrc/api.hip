@@ -135,6 +135,46 @@ harp_status harp_materialize_blocks_q8(const harp_schedule* s, int64_t d, const 
                        "harp_materialize_blocks_q8");
 }
 
+int64_t harp_apply_decode_workspace(const harp_schedule* s, int64_t d, harp_dtype block_dtype, int64_t rows) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err) || !blk_ok(block_dtype) || rows < 0) return -1;
+  return harp::decode_workspace_bytes(pl, static_cast<DT>(block_dtype), rows);
+}
+
+harp_status harp_apply_decode(const harp_schedule* s, int64_t d, const void* blocks, harp_dtype block_dtype,
+                              const float* block_scales, const int8_t* signs, const void* x, int64_t ldx,
+                              void* y, int64_t ldy, int64_t rows, harp_dtype io_dtype, int32_t inverse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err)) return fail(HARP_ERR_INVALID_ARG, err);
+  if (!io_ok(io_dtype)) return fail(HARP_ERR_UNSUPPORTED, "io_dtype must be HARP_F32 or HARP_BF16");
+  if (!blk_ok(block_dtype)) return fail(HARP_ERR_UNSUPPORTED, "block_dtype must be HARP_F32, HARP_BF16 or HARP_I8");
+  if ((block_dtype == HARP_I8) != (block_scales != nullptr))
+    return fail(HARP_ERR_INVALID_ARG, "block_scales must be given exactly for HARP_I8 blocks");
+  if (rows > HARP_DECODE_MAX_ROWS)
+    return fail(HARP_ERR_INVALID_ARG, "harp_apply_decode takes at most HARP_DECODE_MAX_ROWS rows; use harp_apply");
+  const int eb = io_dtype == HARP_F32 ? 4 : 2;
+  err = harp::check_rows(x, ldx, y, ldy, rows, d, eb);
+  if (!err.empty()) return fail(HARP_ERR_INVALID_ARG, err);
+  const int64_t need = harp::decode_workspace_bytes(pl, static_cast<DT>(block_dtype), rows);
+  if (need < 0) return fail(HARP_ERR_UNSUPPORTED, "no split of this schedule into two digit runs fits a workgroup");
+  if (rows == 0) return HARP_OK;
+  if (blocks == nullptr) return fail(HARP_ERR_INVALID_ARG, "blocks is NULL");
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < (size_t)need)
+      return fail(HARP_ERR_INVALID_ARG, "workspace missing or smaller than harp_apply_decode_workspace()");
+    if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+      return fail(HARP_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+  }
+  const DT io = static_cast<DT>(io_dtype);
+  return launch_status(harp::launch_apply_decode(pl, inverse != 0, blocks, static_cast<DT>(block_dtype), block_scales,
+                                                 signs, x, ldx, io, y, ldy, rows, static_cast<float*>(workspace),
+                                                 stream),
+                       "harp_apply_decode");
+}
+
 harp_status harp_apply(const harp_schedule* s, int64_t d, const void* blocks, harp_dtype block_dtype,
                        const float* block_scales, const int8_t* signs, const void* x, int64_t ldx,
                        void* y, int64_t ldy, int64_t rows, harp_dtype io_dtype, hipStream_t stream) {

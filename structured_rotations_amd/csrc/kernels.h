@@ -60,6 +60,14 @@ hipError_t launch_materialize(const Plan& pl, const double* theta, const int8_t*
                               const float* tscale, const double* gauss, DT bdt, void* blocks,
                               float* scales, hipStream_t stream);
 
+// Small-batch apply: two launches over digit runs (fp32 rows in ws between
+// them) or one.  decode_workspace_bytes: ws bytes needed (0 for one launch),
+// -1 if no digit split fits a workgroup.
+int64_t decode_workspace_bytes(const Plan& pl, DT bdt, int64_t rows);
+hipError_t launch_apply_decode(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
+                               const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
+                               int64_t rows, float* ws, hipStream_t stream);
+
 // int8 codes + one fp32 scale per stage of fp64 theta.
 hipError_t launch_quantize_theta(const Plan& pl, const double* theta, int8_t* codes, float* scales,
                                  hipStream_t stream);

@@ -166,3 +166,32 @@ def test_status_strings(lib):
     assert lib.harp_status_str(-2) == b"HARP_ERR_UNSUPPORTED"
     assert lib.harp_status_str(-3) == b"HARP_ERR_LAUNCH"
     assert lib.harp_version().startswith(b"harp-gfx950")
+
+
+def test_decode_workspace_sizes_on_host(lib):
+    ws = lib.harp_apply_decode_workspace
+    assert ws(ctypes.byref(Schedule.of((8, 8, 8, 8))), 4096, _lib.HARP_F32, 3) == 3 * 4096 * 4
+    assert ws(ctypes.byref(Schedule.of((8, 8, 8, 5, 2))), 5120, _lib.HARP_BF16, 64) == 64 * 5120 * 4
+    assert ws(ctypes.byref(Schedule.of((8, 8))), 64, _lib.HARP_F32, 5) == 0      # one launch
+    assert ws(ctypes.byref(Schedule.of((8, 8))), 65, _lib.HARP_F32, 5) == -1     # not a factorisation
+    assert ws(ctypes.byref(Schedule.of((8, 8))), 64, 7, 5) == -1                 # bad dtype
+
+
+def test_decode_rejects_on_host(lib):
+    s = ctypes.byref(Schedule.of((8, 8, 8, 8)))
+    dec = lib.harp_apply_decode
+    # rows above the maximum
+    assert dec(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 1025, 1, 0, FAKE, 1 << 30, None) == \
+        _lib.HARP_ERR_INVALID_ARG
+    # workspace missing / too small
+    assert dec(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 2, 1, 0, None, 0, None) == \
+        _lib.HARP_ERR_INVALID_ARG
+    assert dec(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 2, 1, 0, FAKE, 2 * 4096 * 4 - 1, None) == \
+        _lib.HARP_ERR_INVALID_ARG
+    # int8 blocks without scales, bad io dtype
+    assert dec(s, 4096, FAKE, 2, None, None, FAKE, 4096, FAKE2, 4096, 2, 1, 0, FAKE, 1 << 20, None) == \
+        _lib.HARP_ERR_INVALID_ARG
+    assert dec(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 2, 2, 0, FAKE, 1 << 20, None) == \
+        _lib.HARP_ERR_UNSUPPORTED
+    # zero rows: no launch, OK
+    assert dec(s, 4096, None, 0, None, None, None, 4096, None, 4096, 0, 1, 0, None, 0, None) == _lib.HARP_OK
