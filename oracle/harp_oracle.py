@@ -47,7 +47,7 @@ __all__ = [
     "is_pow2", "sylvester", "qr_fallback", "mgs_qr", "givens", "cayley",
     "theta_counts", "gauss_stage_list", "materialize_blocks", "stage_strides",
     "theta_groups", "quantize_theta", "dequantize_theta",
-    "apply", "apply_inverse", "dense_operator", "fwht", "rht_compose",
+    "apply", "apply_inverse", "apply_vjp", "theta_vjp", "dense_operator", "fwht", "rht_compose",
     "rotate_weight", "round_bf16", "round_f32", "quantize_i8", "stored_blocks",
     "row_rel_l2", "unpack_bf16",
 ]
@@ -309,6 +309,88 @@ def apply_inverse(y: np.ndarray, schedule, blocks, signs=None) -> np.ndarray:
     if signs is not None:
         y = y * np.asarray(signs, dtype=np.float64)[None, :]
     return y[0] if squeeze else y
+
+
+def _groups(x: np.ndarray, schedule, t: int) -> np.ndarray:
+    """(rows, groups, b_t) copy of x: digit t last, group c the C-order index of
+    the other digits (readings R1, R2)."""
+    rows = x.shape[0]
+    m = len(schedule)
+    v = np.moveaxis(x.reshape((rows,) + tuple(schedule)), 1 + t, m)
+    return v.reshape(rows, -1, schedule[t])
+
+
+def apply_vjp(x: np.ndarray, schedule, blocks, signs, dy: np.ndarray):
+    """Reverse-mode derivative of the forward transform against an upstream
+    gradient dy (one per row), for fitting Theta by gradient descent on a
+    calibration loss [TS §2.3].  For L = sum over rows of <dy, y>,
+    y = S_{m-1} ... S_0 D_s x:
+
+      x_0 = D_s x, x_{t+1} = S_t x_t;  g_m = dy, g_t = S_t^T g_{t+1};
+      dL/dB_{t,c}[r, k] = sum over rows of g_{t+1}[c, r] x_t[c, k];
+      dL/dx = D_s g_0.
+
+    Returns (dx, dblocks) with dblocks[t] shaped like blocks[t]."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    dy = np.atleast_2d(np.asarray(dy, dtype=np.float64))
+    d = x.shape[1]
+    _check_schedule(schedule, d)
+    s = np.ones(d) if signs is None else np.asarray(signs, dtype=np.float64)
+    acts = []
+    v = x * s[None, :]
+    for t in range(len(schedule)):
+        acts.append(v)
+        v = _stage(v, schedule, t, blocks[t], transpose=False)
+    g = dy
+    dblocks = [None] * len(schedule)
+    for t in reversed(range(len(schedule))):
+        gv = _groups(g, schedule, t)
+        xv = _groups(acts[t], schedule, t)
+        dblocks[t] = np.einsum("ncr,nck->crk", gv, xv)
+        g = _stage(g, schedule, t, blocks[t], transpose=True)
+    return g * s[None, :], dblocks
+
+
+def theta_vjp(schedule, d: int, theta: np.ndarray, gauss: np.ndarray | None, dblocks):
+    """Chain dL/dB_{t,c} back to the parameters through B = Q(theta) G
+    [TS §2.2]: dL/dQ = dL/dB G^T, then
+
+      Givens (R9):  dQ/dtheta = [[-sin, -cos], [cos, -sin]];
+      Cayley (R8):  Q = (I - A) M with M = (I + A)^-1, so
+                    dQ = -(I + Q) dA M and dL/dA = -(I + Q)^T (dL/dQ) M^T;
+                    A is U - U^T with U's strict upper triangle the group's
+                    parameters (row-major), so dL/dtheta_(r,k) = dL/dA[r,k] - dL/dA[k,r].
+
+    Returns dtheta in theta's layout."""
+    _check_schedule(schedule, d)
+    theta = np.asarray(theta, dtype=np.float64).ravel()
+    gauss = np.zeros(0) if gauss is None else np.asarray(gauss, dtype=np.float64).ravel()
+    out = np.zeros_like(theta)
+    tpos = gpos = 0
+    for t, b in enumerate(schedule):
+        if is_pow2(b):
+            g = sylvester(b)
+        else:
+            g = qr_fallback(gauss[gpos:gpos + b * b].reshape(b, b))
+            gpos += b * b
+        ngroups = d // b
+        per = 1 if b == 2 else b * (b - 1) // 2
+        iu = np.triu_indices(b, k=1)
+        for c in range(ngroups):
+            gq = np.asarray(dblocks[t][c], dtype=np.float64) @ g.T
+            th = theta[tpos + c * per: tpos + (c + 1) * per]
+            if b == 2:
+                cs, sn = np.cos(th[0]), np.sin(th[0])
+                out[tpos + c] = np.sum(gq * np.array([[-sn, -cs], [cs, -sn]]))
+            else:
+                a = skew_from_params(th, b)
+                eye = np.eye(b)
+                minv = np.linalg.inv(eye + a)
+                q = (eye - a) @ minv
+                da = -(eye + q).T @ gq @ minv.T
+                out[tpos + c * per: tpos + (c + 1) * per] = da[iu] - da.T[iu]
+        tpos += ngroups * per
+    return out
 
 
 def dense_operator(schedule, blocks, signs=None) -> np.ndarray:

@@ -496,3 +496,124 @@ def test_theta_i8_zero_and_cayley_lipschitz():
             pos += per
             bound = 2 * np.linalg.norm(da, 2)
             assert np.linalg.norm(b1[t][c] - b0[t][c], 2) <= bound * 1.05 + 1e-15
+
+
+# ------------------------------------------------------------------ reverse mode (calibration gradients)
+def _vjp_case(sch, d, rows, seed, sigma=0.2):
+    rng = np.random.default_rng(seed)
+    theta = rng.standard_normal(sum(O.theta_counts(sch, d))) * sigma
+    gl = O.gauss_stage_list(sch)
+    gauss = np.concatenate([rng.standard_normal(sch[t] ** 2) for t in gl]) if gl else None
+    signs = rng.choice([-1.0, 1.0], d)
+    x = rng.standard_normal((rows, d))
+    dy = rng.standard_normal((rows, d))
+    return theta, gauss, signs, x, dy
+
+
+@pytest.mark.parametrize("sch,d", [((2, 3, 4), 24), ((8, 8), 64), ((5, 2), 10)])
+def test_vjp_dx_is_transpose_apply(sch, d):
+    # dL/dx = M^T dy; M is orthogonal [TS §2.1], so this is also the inverse
+    # transform and the dense operator's transpose times dy.
+    theta, gauss, signs, x, dy = _vjp_case(sch, d, 3, 11)
+    blocks = O.materialize_blocks(sch, d, theta, gauss)
+    dx, _ = O.apply_vjp(x, sch, blocks, signs, dy)
+    m = O.dense_operator(sch, blocks, signs)
+    np.testing.assert_allclose(dx, dy @ m, atol=1e-12)
+    np.testing.assert_allclose(dx, O.apply_inverse(dy, sch, blocks, signs), atol=1e-12)
+
+
+@pytest.mark.parametrize("sch,d", [((2, 3, 4), 24), ((3, 2), 6)])
+def test_vjp_dblocks_central_differences(sch, d):
+    # y is linear in each single block entry, so a central difference of
+    # L = sum <dy, y> in that entry is exact up to rounding.
+    theta, gauss, signs, x, dy = _vjp_case(sch, d, 4, 12)
+    blocks = O.materialize_blocks(sch, d, theta, gauss)
+    _, dblocks = O.apply_vjp(x, sch, blocks, signs, dy)
+    h = 0.5
+    for t in range(len(sch)):
+        for idx in np.ndindex(blocks[t].shape):
+            bp = [b.copy() for b in blocks]
+            bm = [b.copy() for b in blocks]
+            bp[t][idx] += h
+            bm[t][idx] -= h
+            fd = (np.sum(dy * O.apply(x, sch, bp, signs)) - np.sum(dy * O.apply(x, sch, bm, signs))) / (2 * h)
+            assert abs(fd - dblocks[t][idx]) <= 1e-11 * max(1.0, abs(fd)), (t, idx)
+
+
+@pytest.mark.parametrize("sch,d", [((2, 3, 4), 24), ((5, 2), 10), ((4, 4), 16)])
+def test_theta_vjp_central_differences(sch, d):
+    # The whole chain theta -> blocks -> y against central differences of the
+    # oracle forward: O(h^2) truncation, h = 1e-5.
+    theta, gauss, signs, x, dy = _vjp_case(sch, d, 3, 13)
+    blocks = O.materialize_blocks(sch, d, theta, gauss)
+    _, dblocks = O.apply_vjp(x, sch, blocks, signs, dy)
+    dtheta = O.theta_vjp(sch, d, theta, gauss, dblocks)
+
+    def loss(th):
+        return np.sum(dy * O.apply(x, sch, O.materialize_blocks(sch, d, th, gauss), signs))
+    h = 1e-5
+    for i in range(theta.size):
+        tp, tm = theta.copy(), theta.copy()
+        tp[i] += h
+        tm[i] -= h
+        fd = (loss(tp) - loss(tm)) / (2 * h)
+        assert abs(fd - dtheta[i]) <= 1e-7 * max(1.0, abs(fd)), i
+
+
+def test_theta_vjp_matches_torch_autograd():
+    # The theta -> block map differentiated by torch's autograd (fp64, CPU):
+    # Cayley by a linear solve, Givens by cos/sin, times the same base G.
+    sch, d = (4, 2, 3), 24
+    theta, gauss, _, _, _ = _vjp_case(sch, d, 1, 14)
+    rng = np.random.default_rng(15)
+    dblocks = [rng.standard_normal((d // b, b, b)) for b in sch]
+    want = O.theta_vjp(sch, d, theta, gauss, dblocks)
+    th = torch.tensor(theta, dtype=torch.float64, requires_grad=True)
+    loss = torch.zeros((), dtype=torch.float64)
+    pos = gpos = 0
+    for t, b in enumerate(sch):
+        if O.is_pow2(b):
+            g = torch.tensor(O.sylvester(b))
+        else:
+            g = torch.tensor(O.qr_fallback(gauss[gpos:gpos + b * b].reshape(b, b)))
+            gpos += b * b
+        per = 1 if b == 2 else b * (b - 1) // 2
+        for c in range(d // b):
+            p = th[pos + c * per: pos + (c + 1) * per]
+            if b == 2:
+                cs, sn = torch.cos(p[0]), torch.sin(p[0])
+                q = torch.stack([torch.stack([cs, -sn]), torch.stack([sn, cs])])
+            else:
+                u = torch.zeros(b, b, dtype=torch.float64)
+                iu = torch.triu_indices(b, b, 1)
+                u = u.index_put((iu[0], iu[1]), p)
+                a = u - u.T
+                eye = torch.eye(b, dtype=torch.float64)
+                q = torch.linalg.solve(eye + a, eye - a)
+            loss = loss + torch.sum(torch.tensor(dblocks[t][c]) * (q @ g))
+        pos += (d // b) * per
+    loss.backward()
+    np.testing.assert_allclose(want, th.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_theta_vjp_at_zero_closed_form():
+    # At theta = 0: Q = I and M = I, so dL/dA = -2 dL/dQ and
+    # dtheta_(r,k) = -2 (dQ[r,k] - dQ[k,r]) for Cayley; for Givens
+    # dtheta = dQ[1,0] - dQ[0,1]; dQ = dB G^T.
+    sch, d = (4, 2), 8
+    rng = np.random.default_rng(16)
+    dblocks = [rng.standard_normal((d // b, b, b)) for b in sch]
+    dt = O.theta_vjp(sch, d, np.zeros(sum(O.theta_counts(sch, d))), None, dblocks)
+    g4 = scipy.linalg.hadamard(4) / 2.0
+    g2 = scipy.linalg.hadamard(2) / np.sqrt(2.0)
+    pos = 0
+    for c in range(2):
+        gq = dblocks[0][c] @ g4.T
+        for r in range(4):
+            for k in range(r + 1, 4):
+                assert abs(dt[pos] - (-2.0) * (gq[r, k] - gq[k, r])) < 1e-12
+                pos += 1
+    for c in range(4):
+        gq = dblocks[1][c] @ g2.T
+        assert abs(dt[pos] - (gq[1, 0] - gq[0, 1])) < 1e-12
+        pos += 1
