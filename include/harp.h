@@ -213,6 +213,49 @@ harp_status harp_apply_decode(const harp_schedule* s, int64_t d,
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Reverse mode, for fitting the parameters on calibration data   [TS §2.3:
+ * the parameters are fitted per layer by minimising a calibration loss;
+ * TS §2.1-§2.2 for the transform being differentiated]
+ *
+ * harp_apply_vjp: for y = S_{m-1} ... S_0 D_s x (as harp_apply) and an
+ *   upstream gradient dy (rows x d, same dtype and layout rules as x):
+ *     dx      = D_s S_0^T ... S_{m-1}^T dy          (skipped if dx is NULL)
+ *     dblocks = dL/dB_{t,c}[r][k] = sum over rows of g_{t+1}[c, r] x_t[c, k],
+ *               with x_0 = D_s x, x_{t+1} = S_t x_t, g_m = dy,
+ *               g_t = S_t^T g_{t+1};  harp_block_count() fp32 values in the
+ *               block layout, overwritten.  The derivative is taken with
+ *               respect to the block values actually multiplied by (for I8
+ *               blocks, code * scale).
+ *   Arithmetic in fp32; the sum over rows runs in chunks whose partial sums
+ *   are added in a fixed order, so the result is deterministic.
+ *   workspace: at least harp_apply_vjp_workspace() bytes of device memory,
+ *   4-byte aligned, owned by the caller (x_1 .. x_{m-1} and two gradient rows
+ *   in fp32, plus the partial sums).  Every radix must be at most 8 (else
+ *   HARP_ERR_UNSUPPORTED, and harp_apply_vjp_workspace() returns -1).
+ *   rows must be at least 1.
+ * harp_theta_vjp: dtheta (harp_theta_count() fp64, theta's layout) from
+ *   dblocks through B = Q(theta) G: dL/dQ = dL/dB G^T; Givens
+ *   dQ/dtheta = [[-sin, -cos], [cos, -sin]]; Cayley Q = (I - A)(I + A)^-1 gives
+ *   dL/dA = -(I + Q)^T (dL/dQ) (I + A)^-T and
+ *   dL/dtheta_(r,k) = dL/dA[r][k] - dL/dA[k][r].  fp64 on the device; theta
+ *   and gauss as harp_materialize_blocks.
+ * ---------------------------------------------------------------------- */
+int64_t harp_apply_vjp_workspace(const harp_schedule* s, int64_t d,
+                                 int64_t rows);
+harp_status harp_apply_vjp(const harp_schedule* s, int64_t d,
+                           const void* blocks, harp_dtype block_dtype,
+                           const float* block_scales, const int8_t* signs,
+                           const void* x, int64_t ldx, const void* dy,
+                           int64_t lddy, void* dx, int64_t lddx, int64_t rows,
+                           harp_dtype io_dtype, float* dblocks,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+harp_status harp_theta_vjp(const harp_schedule* s, int64_t d,
+                           const double* theta, const double* gauss,
+                           const float* dblocks, double* dtheta,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Two-sided weight rotation [TS §2, §3; ABS: a two-sided processor]
  *   inverse == 0:  W_out = M_U W M_V^T      (M_V on every row of W,
  *                                           M_U on every column)

@@ -59,6 +59,10 @@ _SIG = {
     "harp_apply_inverse": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64, _I64,
                                   _I32, _P]),
     "harp_rotate_weight_workspace": (ctypes.c_size_t, [_I64, _I64]),
+    "harp_apply_vjp_workspace": (_I64, [ctypes.POINTER(Schedule), _I64, _I64]),
+    "harp_apply_vjp": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64, _P, _I64, _I64,
+                              _I32, _P, _P, ctypes.c_size_t, _P]),
+    "harp_theta_vjp": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _P, _P, _P, _P]),
     "harp_apply_decode_workspace": (_I64, [ctypes.POINTER(Schedule), _I64, _I32, _I64]),
     "harp_apply_decode": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64, _I64, _I32,
                                  _I32, _P, ctypes.c_size_t, _P]),

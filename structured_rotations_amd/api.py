@@ -205,6 +205,59 @@ def harp_apply_decode(schedule, d: int, blocks, scales, signs, x, y=None, invers
     return y
 
 
+def harp_apply_vjp_workspace(schedule, d: int, rows: int) -> int:
+    """Workspace bytes harp_apply_vjp needs (-1: a radix above 8)."""
+    return int(lib().harp_apply_vjp_workspace(ctypes.byref(Schedule.of(schedule)), d, rows))
+
+
+def harp_apply_vjp(schedule, d: int, blocks, scales, signs, x, dy, dx=None, want_dx: bool = True,
+                   dblocks=None, workspace=None, stream=None):
+    """Reverse mode of harp_apply for an upstream gradient dy: returns
+    (dx or None, dblocks), dblocks fp32 in the block layout."""
+    for n, t in (("blocks", blocks), ("scales", scales), ("signs", signs), ("x", x), ("dy", dy),
+                 ("dx", dx), ("dblocks", dblocks), ("workspace", workspace)):
+        _dev(t, n)
+    rows, ldx = _rows_ld(x, d, "x")
+    rows_g, lddy = _rows_ld(dy, d, "dy")
+    if rows_g != rows or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in rows and dtype")
+    if signs is not None and signs.dtype != torch.int8:
+        raise TypeError("signs must be int8")
+    if dx is None and want_dx:
+        dx = torch.empty_like(x)
+    lddx = 0
+    if dx is not None:
+        rows_d, lddx = _rows_ld(dx, d, "dx")
+        if rows_d != rows or dx.dtype != x.dtype:
+            raise ValueError("dx must match x in rows and dtype")
+    if dblocks is None:
+        dblocks = torch.empty(harp_block_count(schedule, d), dtype=torch.float32, device=x.device)
+    sch = Schedule.of(schedule)
+    if workspace is None:
+        need = int(lib().harp_apply_vjp_workspace(ctypes.byref(sch), d, rows))
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib().harp_apply_vjp(ctypes.byref(sch), d, _ptr(blocks), _DT[blocks.dtype], _ptr(scales), _ptr(signs),
+                               _ptr(x), ldx, _ptr(dy), lddy, _ptr(dx), lddx, rows, _DT[x.dtype], _ptr(dblocks),
+                               _ptr(workspace), ws_bytes, _stream(stream)))
+    return dx, dblocks
+
+
+def harp_theta_vjp(schedule, d: int, theta: torch.Tensor, gauss, dblocks, dtheta=None, stream=None):
+    """dL/dtheta (fp64, theta's layout) from dL/dB (fp32 block layout)."""
+    for n, t in (("theta", theta), ("gauss", gauss), ("dblocks", dblocks), ("dtheta", dtheta)):
+        _dev(t, n)
+    if theta.dtype != torch.float64 or (gauss is not None and gauss.dtype != torch.float64):
+        raise TypeError("theta and gauss must be float64")
+    if dblocks.dtype != torch.float32 or dblocks.numel() != harp_block_count(schedule, d):
+        raise ValueError("dblocks must be float32 with harp_block_count() elements")
+    if dtheta is None:
+        dtheta = torch.empty_like(theta)
+    check(lib().harp_theta_vjp(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta), _ptr(gauss), _ptr(dblocks),
+                               _ptr(dtheta), _stream(stream)))
+    return dtheta
+
+
 def harp_rotate_weight(su, blocks_u, scales_u, signs_u, sv, blocks_v, scales_v, signs_v, w,
                        w_out=None, inverse: bool = False, workspace=None, stream=None):
     """W_out = M_U W M_V^T (inverse: M_U^T W M_V); W is prod(su) x prod(sv)."""

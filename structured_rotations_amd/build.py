@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libharp.so")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-HIP_SOURCES = ["api.hip", "apply_tile.hip", "apply_mfma.hip", "apply_valu.hip", "apply_fast.hip", "rht.hip", "rotate_cols.hip", "materialize.hip", "decode.hip"]
+HIP_SOURCES = ["api.hip", "apply_tile.hip", "apply_mfma.hip", "apply_valu.hip", "apply_fast.hip", "rht.hip", "rotate_cols.hip", "materialize.hip", "decode.hip", "vjp.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 DEVICE_FLAGS = [

@@ -175,6 +175,60 @@ harp_status harp_apply_decode(const harp_schedule* s, int64_t d, const void* blo
                        "harp_apply_decode");
 }
 
+int64_t harp_apply_vjp_workspace(const harp_schedule* s, int64_t d, int64_t rows) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err) || rows < 0) return -1;
+  return harp::vjp_workspace_bytes(pl, rows);
+}
+
+harp_status harp_apply_vjp(const harp_schedule* s, int64_t d, const void* blocks, harp_dtype block_dtype,
+                           const float* block_scales, const int8_t* signs, const void* x, int64_t ldx,
+                           const void* dy, int64_t lddy, void* dx, int64_t lddx, int64_t rows,
+                           harp_dtype io_dtype, float* dblocks, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err)) return fail(HARP_ERR_INVALID_ARG, err);
+  if (!io_ok(io_dtype)) return fail(HARP_ERR_UNSUPPORTED, "io_dtype must be HARP_F32 or HARP_BF16");
+  if (!blk_ok(block_dtype)) return fail(HARP_ERR_UNSUPPORTED, "block_dtype must be HARP_F32, HARP_BF16 or HARP_I8");
+  if ((block_dtype == HARP_I8) != (block_scales != nullptr))
+    return fail(HARP_ERR_INVALID_ARG, "block_scales must be given exactly for HARP_I8 blocks");
+  const int64_t need = harp::vjp_workspace_bytes(pl, rows < 0 ? 0 : rows);
+  if (need < 0) return fail(HARP_ERR_UNSUPPORTED, "harp_apply_vjp supports radices up to 8");
+  const int eb = io_dtype == HARP_F32 ? 4 : 2;
+  err = harp::check_rows(x, ldx, dy, lddy, rows, d, eb);
+  if (!err.empty()) return fail(HARP_ERR_INVALID_ARG, "x/dy: " + err);
+  if (dx != nullptr) {
+    err = harp::check_rows(dy, lddy, dx, lddx, rows, d, eb);
+    if (!err.empty()) return fail(HARP_ERR_INVALID_ARG, "dx: " + err);
+  }
+  if (dblocks == nullptr) return fail(HARP_ERR_INVALID_ARG, "dblocks is NULL");
+  if (blocks == nullptr) return fail(HARP_ERR_INVALID_ARG, "blocks is NULL");
+  if (rows == 0) return fail(HARP_ERR_INVALID_ARG, "rows must be at least 1");
+  if (workspace == nullptr || workspace_bytes < (size_t)need)
+    return fail(HARP_ERR_INVALID_ARG, "workspace missing or smaller than harp_apply_vjp_workspace()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+    return fail(HARP_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+  return launch_status(harp::launch_apply_vjp(pl, blocks, static_cast<DT>(block_dtype), block_scales, signs, x, ldx,
+                                              dy, lddy, dx, lddx, static_cast<DT>(io_dtype), rows, dblocks,
+                                              workspace, stream),
+                       "harp_apply_vjp");
+}
+
+harp_status harp_theta_vjp(const harp_schedule* s, int64_t d, const double* theta, const double* gauss,
+                           const float* dblocks, double* dtheta, hipStream_t stream) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err)) return fail(HARP_ERR_INVALID_ARG, err);
+  if (theta == nullptr) return fail(HARP_ERR_INVALID_ARG, "theta is NULL");
+  if (pl.n_gauss > 0 && gauss == nullptr)
+    return fail(HARP_ERR_INVALID_ARG, "gauss is NULL but the schedule has a non-power-of-two radix");
+  if (dblocks == nullptr) return fail(HARP_ERR_INVALID_ARG, "dblocks is NULL");
+  if (dtheta == nullptr) return fail(HARP_ERR_INVALID_ARG, "dtheta is NULL");
+  return launch_status(harp::launch_theta_vjp(pl, theta, gauss, dblocks, dtheta, stream), "harp_theta_vjp");
+}
+
 harp_status harp_apply(const harp_schedule* s, int64_t d, const void* blocks, harp_dtype block_dtype,
                        const float* block_scales, const int8_t* signs, const void* x, int64_t ldx,
                        void* y, int64_t ldy, int64_t rows, harp_dtype io_dtype, hipStream_t stream) {

@@ -68,6 +68,16 @@ hipError_t launch_apply_decode(const Plan& pl, bool inverse, const void* blocks,
                                const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
                                int64_t rows, float* ws, hipStream_t stream);
 
+// Reverse mode of the row transform: dx (optional) and dL/dB for every block
+// (fp32, overwritten).  ws: vjp_workspace_bytes(); -1 if a radix exceeds 8.
+int64_t vjp_workspace_bytes(const Plan& pl, int64_t rows);
+hipError_t launch_apply_vjp(const Plan& pl, const void* blocks, DT bdt, const float* scales, const int8_t* signs,
+                            const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx, int64_t lddx,
+                            DT io, int64_t rows, float* dblocks, void* ws, hipStream_t stream);
+// dL/dtheta from dL/dB (fp64 per group).
+hipError_t launch_theta_vjp(const Plan& pl, const double* theta, const double* gauss, const float* dblocks,
+                            double* dtheta, hipStream_t stream);
+
 // int8 codes + one fp32 scale per stage of fp64 theta.
 hipError_t launch_quantize_theta(const Plan& pl, const double* theta, int8_t* codes, float* scales,
                                  hipStream_t stream);

@@ -159,6 +159,93 @@ __global__ void __launch_bounds__(256) materialize_kernel(MatParams p) {
   }
 }
 
+// Parameter gradient from block gradients, one thread per group, fp64:
+// dL/dQ = dL/dB G^T; Givens: dQ/dtheta = [[-sin, -cos], [cos, -sin]];
+// Cayley Q = (I - A) M with M = (I + A)^-1: dL/dA = -(I + Q)^T (dL/dQ) M^T and
+// dL/dtheta_(r,k) = dL/dA[r][k] - dL/dA[k][r] (A = U - U^T, U row-major from
+// the parameters).  M comes from the same elimination as the forward map,
+// with the identity as right-hand side.
+template <int B>
+__global__ void __launch_bounds__(256) theta_vjp_kernel(int64_t ngroups, const double* theta, const double* gauss,
+                                                        const float* dblocks, double* dtheta) {
+  __shared__ double g[B * B];
+  if (threadIdx.x == 0) base_mixer<B>(gauss, g);
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= ngroups) return;
+  const float* db = dblocks + c * B * B;
+  double gq[B][B];
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < B; ++i) acc += (double)db[r * B + i] * g[k * B + i];
+      gq[r][k] = acc;
+    }
+  if (B == 2) {
+    const double th = theta[c];
+    const double cs = cos(th), sn = sin(th);
+    dtheta[c] = -sn * gq[0][0] - cs * gq[0][1] + cs * gq[1][0] - sn * gq[1][1];
+    return;
+  }
+  constexpr int per = B * (B - 1) / 2;
+  const double* th = theta + c * per;
+  double a[B][B], mtx[B][B], minv[B][B];
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      a[r][k] = 0.0;
+      minv[r][k] = (r == k) ? 1.0 : 0.0;
+    }
+  int idx = 0;
+  for (int r = 0; r < B; ++r)
+    for (int k = r + 1; k < B; ++k) {
+      a[r][k] = th[idx];
+      a[k][r] = -th[idx];
+      ++idx;
+    }
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) mtx[r][k] = (r == k ? 1.0 : 0.0) + a[r][k];
+  for (int k = 0; k < B; ++k) {
+    const double inv = 1.0 / mtx[k][k];
+    for (int i = k + 1; i < B; ++i) {
+      const double f = mtx[i][k] * inv;
+      if (f == 0.0) continue;
+      for (int j = k; j < B; ++j) mtx[i][j] -= f * mtx[k][j];
+      for (int j = 0; j < B; ++j) minv[i][j] -= f * minv[k][j];
+    }
+  }
+  for (int k = B - 1; k >= 0; --k)
+    for (int j = 0; j < B; ++j) {
+      double acc = minv[k][j];
+      for (int i = k + 1; i < B; ++i) acc -= mtx[k][i] * minv[i][j];
+      minv[k][j] = acc / mtx[k][k];
+    }
+  // P = (I + Q) = I + (I - A) M, reusing mtx
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      double acc = (r == k) ? 1.0 : 0.0;
+      for (int i = 0; i < B; ++i) acc += ((r == i ? 1.0 : 0.0) - a[r][i]) * minv[i][k];
+      mtx[r][k] = acc;
+    }
+  // T = gq M^T, reusing a
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < B; ++i) acc += gq[r][i] * minv[k][i];
+      a[r][k] = acc;
+    }
+  // dA = -P^T T, reusing gq
+  for (int r = 0; r < B; ++r)
+    for (int k = 0; k < B; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < B; ++i) acc += mtx[i][r] * a[i][k];
+      gq[r][k] = -acc;
+    }
+  double* out = dtheta + c * per;
+  idx = 0;
+  for (int r = 0; r < B; ++r)
+    for (int k = r + 1; k < B; ++k) out[idx++] = gq[r][k] - gq[k][r];
+}
+
 // One workgroup per stage: scale = fp32(max|theta of the stage| / 127), code =
 // clamp(rint(theta / scale), -127, 127) decided in fp64; a zero stage -> 0, 0.
 constexpr int kQThreads = 1024;
@@ -222,6 +309,49 @@ hipError_t launch_materialize(const Plan& pl, const double* theta, const int8_t*
       case 14: e = launch_mat<14>(p, stream); break;
       case 15: e = launch_mat<15>(p, stream); break;
       case 16: e = launch_mat<16>(p, stream); break;
+      default: e = hipErrorInvalidValue; break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+namespace {
+template <int B>
+hipError_t launch_tvjp(int64_t ng, const double* theta, const double* gauss, const float* db, double* dt,
+                       hipStream_t st) {
+  const int threads = 256;
+  const int64_t grid = (ng + threads - 1) / threads;
+  hipLaunchKernelGGL(theta_vjp_kernel<B>, dim3((unsigned)grid), dim3(threads), 0, st, ng, theta, gauss, db, dt);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_theta_vjp(const Plan& pl, const double* theta, const double* gauss, const float* dblocks,
+                            double* dtheta, hipStream_t stream) {
+  for (int t = 0; t < pl.m; ++t) {
+    const int64_t ng = pl.d / pl.radix[t];
+    const double* th = theta + pl.theta_off[t];
+    const double* gs = pl.gauss_off[t] >= 0 ? gauss + pl.gauss_off[t] : nullptr;
+    const float* db = dblocks + pl.blk_off[t];
+    double* dt = dtheta + pl.theta_off[t];
+    hipError_t e = hipSuccess;
+    switch (pl.radix[t]) {
+      case 2: e = launch_tvjp<2>(ng, th, gs, db, dt, stream); break;
+      case 3: e = launch_tvjp<3>(ng, th, gs, db, dt, stream); break;
+      case 4: e = launch_tvjp<4>(ng, th, gs, db, dt, stream); break;
+      case 5: e = launch_tvjp<5>(ng, th, gs, db, dt, stream); break;
+      case 6: e = launch_tvjp<6>(ng, th, gs, db, dt, stream); break;
+      case 7: e = launch_tvjp<7>(ng, th, gs, db, dt, stream); break;
+      case 8: e = launch_tvjp<8>(ng, th, gs, db, dt, stream); break;
+      case 9: e = launch_tvjp<9>(ng, th, gs, db, dt, stream); break;
+      case 10: e = launch_tvjp<10>(ng, th, gs, db, dt, stream); break;
+      case 11: e = launch_tvjp<11>(ng, th, gs, db, dt, stream); break;
+      case 12: e = launch_tvjp<12>(ng, th, gs, db, dt, stream); break;
+      case 13: e = launch_tvjp<13>(ng, th, gs, db, dt, stream); break;
+      case 14: e = launch_tvjp<14>(ng, th, gs, db, dt, stream); break;
+      case 15: e = launch_tvjp<15>(ng, th, gs, db, dt, stream); break;
+      case 16: e = launch_tvjp<16>(ng, th, gs, db, dt, stream); break;
       default: e = hipErrorInvalidValue; break;
     }
     if (e != hipSuccess) return e;

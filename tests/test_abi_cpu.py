@@ -195,3 +195,28 @@ def test_decode_rejects_on_host(lib):
         _lib.HARP_ERR_UNSUPPORTED
     # zero rows: no launch, OK
     assert dec(s, 4096, None, 0, None, None, None, 4096, None, 4096, 0, 1, 0, None, 0, None) == _lib.HARP_OK
+
+
+def test_vjp_rejects_on_host(lib):
+    s = ctypes.byref(Schedule.of((8, 8, 8, 8)))
+    need = lib.harp_apply_vjp_workspace(s, 4096, 5)
+    assert need > 5 * 4096 * 4 * 5       # three activations + two gradient rows + partial sums
+    assert lib.harp_apply_vjp_workspace(ctypes.byref(Schedule.of((16, 16))), 256, 5) == -1
+    vjp = lib.harp_apply_vjp
+    args = lambda **kw: [s, 4096, kw.get("blocks", FAKE), kw.get("bdt", 0), kw.get("scales", None), None,
+                         FAKE, 4096, FAKE2, 4096, kw.get("dx", None), 4096, kw.get("rows", 5), kw.get("io", 1),
+                         kw.get("dblocks", FAKE), kw.get("ws", FAKE), kw.get("wsb", need), None]
+    assert vjp(*args(ws=None)) == _lib.HARP_ERR_INVALID_ARG
+    assert vjp(*args(wsb=need - 1)) == _lib.HARP_ERR_INVALID_ARG
+    assert vjp(*args(dblocks=None)) == _lib.HARP_ERR_INVALID_ARG
+    assert vjp(*args(rows=0)) == _lib.HARP_ERR_INVALID_ARG
+    assert vjp(*args(bdt=2)) == _lib.HARP_ERR_INVALID_ARG          # int8 without scales
+    assert vjp(*args(io=2)) == _lib.HARP_ERR_UNSUPPORTED
+    s16 = ctypes.byref(Schedule.of((16, 16)))
+    assert vjp(s16, 256, FAKE, 0, None, None, FAKE, 256, FAKE2, 256, None, 256, 5, 1, FAKE, FAKE, 1 << 20,
+               None) == _lib.HARP_ERR_UNSUPPORTED
+    tv = lib.harp_theta_vjp
+    assert tv(s, 4096, None, None, FAKE, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
+    assert tv(s, 4096, FAKE, None, None, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
+    assert tv(s, 4096, FAKE, None, FAKE, None, None) == _lib.HARP_ERR_INVALID_ARG
+    assert tv(ctypes.byref(Schedule.of((8, 5))), 40, FAKE, None, FAKE, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
