@@ -23,6 +23,10 @@ cost included), and of the same calls captured once in a HIP graph and
 replayed (device time per call, launch gaps included); the replay's output is
 checked against the eager calls and both entry points against the oracle.
 
+--mode vjp: the reverse mode used to fit the parameters (dx and the block
+gradients for one batch, then the parameter gradient), milliseconds per call,
+with the HBM bytes its stage-wise design moves.
+
 --mode materialize: microseconds per call of the block materialisation on the
 device from fp64 parameters and from int8 parameter codes, and of the int8
 quantisation of the parameters (setup work, not part of a step).
@@ -213,6 +217,89 @@ def latency_main(args) -> int:
     return 0
 
 
+def vjp_main(args) -> int:
+    """Reverse mode over one batch: harp_apply_vjp (dx + dB) and harp_theta_vjp."""
+    import torch
+
+    from oracle import harp_oracle as O
+    from structured_rotations_amd import api
+    from structured_rotations_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    w = W.make(name)
+    if w["workload"].kind != "apply":
+        print("--mode vjp runs an apply workload", file=sys.stderr)
+        return 2
+    d, sch, io = w["d"], w["schedule"], w["io"]
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    eb = 2 if io == "bf16" else 4
+    x = torch.from_numpy(w["x"]).to(tdt).cuda()
+    rows = x.shape[0]
+    dy = torch.from_numpy(np.random.default_rng(5).standard_normal((rows, d)).astype(np.float32)).to(tdt).cuda()
+    dx = torch.empty_like(x)
+    th = torch.from_numpy(w["theta"]).cuda()
+    gs = torch.from_numpy(w["gauss"]).cuda() if w["gauss"].size else None
+    blocks, scales = api.harp_materialize_blocks(sch, d, th, gs, args.blk)
+    sg = torch.from_numpy(w["signs"]).cuda()
+    nblk = api.harp_block_count(sch, d)
+    db = torch.empty(nblk, dtype=torch.float32, device="cuda")
+    dt = torch.empty_like(th)
+    ws = torch.empty(api.harp_apply_vjp_workspace(sch, d, rows), dtype=torch.uint8, device="cuda")
+    steps = max(args.steps, 3)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_vjp = timed(lambda: api.harp_apply_vjp(sch, d, blocks, scales, sg, x, dy, dx, dblocks=db, workspace=ws))
+    ms_theta = timed(lambda: api.harp_theta_vjp(sch, d, th, gs, db, dt))
+    m = len(sch)
+    rd = rows * d
+    nchunk = (ws.numel() - 4 * rd * ((m - 1) + (2 if m > 1 else 0))) // (4 * nblk)
+    fwd = rd * (eb + 4) + (m - 2) * rd * 8 if m > 1 else 0
+    if m > 1:
+        bwd = rd * (eb + 4 + 4) + (m - 2) * rd * 12 + rd * (4 + eb + eb)
+    else:
+        bwd = rd * 3 * eb
+    red = nchunk * nblk * 4 * 2 + nblk * 4
+    moved = fwd + bwd + red
+    # parity on 4 sampled rows is not defined for a sum over rows; check dx rows instead
+    idx = np.array([0, rows // 2, rows - 1])
+    ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
+    rdx = O.apply_inverse(dy[torch.from_numpy(idx).cuda()].float().cpu().numpy().astype(np.float64), sch, ob,
+                          w["signs"].astype(float))
+    par = float(O.row_rel_l2(dx[torch.from_numpy(idx).cuda()].float().cpu().numpy(), rdx).max())
+    line = {
+        "metric": "HARP reverse mode (dx + block gradients) over one batch, ms per call",
+        "value": round(ms_vjp, 4),
+        "unit": "ms/call",
+        "n_gpus": 1, "steps": steps, "warmup": 2,
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded rows and parameters of the named workload, seeded normal upstream gradient)",
+        "config": {"workload": name, "rows": rows, "d": d, "schedule": list(sch), "io": io, "blocks": args.blk,
+                   "kind": "vjp", "parallelism": "single GPU"},
+        "hbm_bytes_moved_by_design": moved,
+        "achieved_GBps_on_design_bytes": round(moved / (ms_vjp * 1e-3) / 1e9, 1),
+        "io_bytes_x_dy_dx": 3 * rd * eb,
+        "ms_theta_vjp": round(ms_theta, 4),
+        "chunks": int(nchunk),
+        "parity_dx_max_row_rel_l2": par,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def materialize_main(args) -> int:
     """Block materialisation and int8 parameter quantisation, microseconds per call."""
     import torch
@@ -294,7 +381,7 @@ def main() -> int:
                     help="time a plain device copy of the batch instead (counter calibration)")
     ap.add_argument("--flush", action="store_true",
                     help="per-launch timing with L2 and MALL flushed (a 1 GiB write) before every launch")
-    ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize"])
+    ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize", "vjp"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the apply path has no cross-GPU step and this build runs on a "
@@ -304,6 +391,8 @@ def main() -> int:
         return latency_main(args)
     if args.mode == "materialize":
         return materialize_main(args)
+    if args.mode == "vjp":
+        return vjp_main(args)
 
     import torch
 

@@ -22,6 +22,7 @@ namespace harp {
 namespace {
 
 constexpr int kVjpThreads = 256;
+constexpr int64_t kVjpTargetThreads = 262144;   // threads per stage launch (group x row chunk)
 
 struct VjpStage {
   int b, s;           // radix, digit stride
@@ -176,7 +177,7 @@ int vjp_chunks(const Plan& pl, int64_t rows) {
   int64_t ng = pl.d;
   for (int t = 0; t < pl.m; ++t)
     if (pl.d / pl.radix[t] < ng) ng = pl.d / pl.radix[t];
-  int64_t n = (65536 + ng - 1) / ng;
+  int64_t n = (kVjpTargetThreads + ng - 1) / ng;
   if (n > rows) n = rows;
   if (n < 1) n = 1;
   return (int)n;
