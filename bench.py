@@ -48,9 +48,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str) -> str:
     from structured_rotations_amd.build import source_hash
-    return source_hash()
+    return source_hash(kernel)
 
 
 def traffic_from_profile(workload: str, blk: str):
@@ -64,7 +64,7 @@ def traffic_from_profile(workload: str, blk: str):
         rec = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(rec.get("kernel", "")):
         return None
     return rec.get("bytes_per_launch")
 

@@ -36,16 +36,28 @@ DEVICE_FLAGS = [
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC]
 
 
-def source_hash() -> str:
-    """Hash of every kernel and launcher source under csrc/ (counter-measured
-    traffic records name the sources they were measured on)."""
+# The sources each measured kernel is built and launched from: a counter
+# record stays valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "apply_pipe": ["apply_fast.hip", "row_io.h", "common.h"],
+    "apply_5120": ["apply_fast.hip", "row_io.h", "common.h"],
+    "rht_wave": ["rht.hip", "common.h"],
+    "col_pass": ["rotate_cols.hip", "apply_fast.hip", "row_io.h", "common.h", "api.hip"],
+}
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources of one measured kernel (KERNEL_SOURCES), or of every
+    kernel and launcher source under csrc/ when no kernel is named."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    files = KERNEL_SOURCES.get(kernel) if kernel else None
+    if files is None:
+        files = [f for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".h", ".cpp"))]
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 

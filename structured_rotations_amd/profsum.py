@@ -9,8 +9,8 @@
 average of every counter the database holds).  `traffic` turns two counter
 runs of a kernel (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) into HBM
 bytes per launch, each scaled by what the same counter reads for a plain
-device copy of known size, and records it with the hash of the kernel sources
-it was measured on.
+device copy of known size, and records it with the hash of that kernel's sources
+(build.KERNEL_SOURCES) it was measured on.
 """
 from __future__ import annotations
 
@@ -86,7 +86,7 @@ def cmd_traffic(args) -> int:
     f_read, f_write = cf / kib, cw / kib
     traffic = fetch * 1024.0 / f_read + write * 1024.0 / f_write
     rec = {
-        "workload": args.workload, "blk": args.blk, "kernel": args.kernel, "kernel_hash": source_hash(),
+        "workload": args.workload, "blk": args.blk, "kernel": args.kernel, "kernel_hash": source_hash(args.kernel),
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
         "copy_bytes_each_way": args.copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
         "scale_read": f_read, "scale_write": f_write,
