@@ -144,3 +144,28 @@ def test_decode_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager)
+
+
+def test_decode_unaligned_blocks_and_largest_row():
+    # Blocks 4 bytes off a 16-byte boundary take the generic kernel; d = 32768
+    # (the largest row) splits into runs of 64 and 512.
+    sch, d = (8, 8, 8, 8, 8), 32768
+    print(f"\n[case] decode {sch} unaligned blocks", flush=True)
+    g_sign, g_theta, _, g_data = I.streams(I.BASE_SEED + 300)
+    theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
+    signs = I.rademacher(g_sign, d)
+    x = g_data.standard_normal((3, d)).astype(np.float32)
+    blocks_g, _ = gpu_blocks(api, sch, d, theta, None, "f32")
+    shifted = torch.empty(blocks_g.numel() + 1, dtype=torch.float32, device="cuda")[1:]
+    shifted.copy_(blocks_g)
+    assert shifted.data_ptr() % 16 != 0
+    sg = signs_dev(signs)
+    y_al = api.harp_apply_decode(sch, d, blocks_g, None, sg, to_dev(x, "f32"))
+    y_un = api.harp_apply_decode(sch, d, shifted, None, sg, to_dev(x, "f32"))
+    y_ap = api.harp_apply(sch, d, blocks_g, None, sg, to_dev(x, "f32"))
+    torch.cuda.synchronize()
+    blocks_o = oracle_blocks(sch, d, theta, None, "f32")
+    y_ref = O.apply(x.astype(np.float64), sch, blocks_o, signs.astype(float))
+    assert_rows_close(from_dev(y_al), y_ref, TOL["f32"], "aligned")
+    assert_rows_close(from_dev(y_un), y_ref, TOL["f32"], "unaligned")
+    assert_rows_close(from_dev(y_ap), y_ref, TOL["f32"], "harp_apply at d = 32768")
