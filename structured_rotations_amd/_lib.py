@@ -28,14 +28,24 @@ class Schedule(ctypes.Structure):
 
     @classmethod
     def of(cls, radices) -> "Schedule":
-        radices = [int(b) for b in radices]
-        if not 1 <= len(radices) <= MAX_STAGES:
-            raise ValueError(f"a schedule has 1..{MAX_STAGES} stages, got {len(radices)}")
-        s = cls()
-        s.m = len(radices)
-        for i, b in enumerate(radices):
-            s.radix[i] = b
+        """The (shared, read-only) struct for a radix list; the library copies
+        it at call time, so one instance per schedule serves every call."""
+        if isinstance(radices, Schedule):
+            return radices
+        key = tuple(int(b) for b in radices)
+        s = _SCHEDULES.get(key)
+        if s is None:
+            if not 1 <= len(key) <= MAX_STAGES:
+                raise ValueError(f"a schedule has 1..{MAX_STAGES} stages, got {len(key)}")
+            s = cls()
+            s.m = len(key)
+            for i, b in enumerate(key):
+                s.radix[i] = b
+            _SCHEDULES[key] = s
         return s
+
+
+_SCHEDULES: dict = {}
 
 
 class HarpError(RuntimeError):
