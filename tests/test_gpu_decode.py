@@ -169,3 +169,17 @@ def test_decode_unaligned_blocks_and_largest_row():
     assert_rows_close(from_dev(y_al), y_ref, TOL["f32"], "aligned")
     assert_rows_close(from_dev(y_un), y_ref, TOL["f32"], "unaligned")
     assert_rows_close(from_dev(y_ap), y_ref, TOL["f32"], "harp_apply at d = 32768")
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+def test_decode_without_signs(inverse):
+    # signs = NULL is D_s = I on both entry points.
+    w = _case("mixed5120_bf16", 3)
+    sch, d = w["schedule"], w["d"]
+    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    x = to_dev(w["x"], "f32")
+    y = api.harp_apply_decode(sch, d, blocks_g, None, None, x, inverse=inverse)
+    torch.cuda.synchronize()
+    blocks_o = oracle_blocks(sch, d, w["theta"], w["gauss"], "f32")
+    fn = O.apply_inverse if inverse else O.apply
+    assert_rows_close(from_dev(y), fn(w["x"].astype(np.float64), sch, blocks_o, None), TOL["f32"], "no signs")

@@ -142,3 +142,17 @@ def test_vjp_errors_and_no_dx():
     with pytest.raises(HarpError):
         api.harp_apply_vjp(sch, d, blocks_g, None, sg, x, x, workspace=ws[:need - 4])
     assert api.harp_apply_vjp_workspace((16, 16), 256, 3) == -1
+
+
+def test_vjp_without_signs_and_one_row():
+    w = W.make("cayley4096_bf16", 1)
+    sch, d = w["schedule"], w["d"]
+    print("\n[case] vjp cayley4096 rows=1 no signs", flush=True)
+    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    dy = _dy(1, d, "f32", 8)
+    dx, db = api.harp_apply_vjp(sch, d, blocks_g, None, None, to_dev(w["x"], "f32"), to_dev(dy, "f32"))
+    torch.cuda.synchronize()
+    blocks_o = oracle_blocks(sch, d, w["theta"], w["gauss"], "f32")
+    rdx, rdb = O.apply_vjp(w["x"].astype(np.float64), sch, blocks_o, None, dy.astype(np.float64))
+    assert_rows_close(from_dev(dx), rdx, TOL["f32"], "dx")
+    _assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, "dB")
