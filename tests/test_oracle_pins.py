@@ -617,3 +617,32 @@ def test_theta_vjp_at_zero_closed_form():
         gq = dblocks[1][c] @ g2.T
         assert abs(dt[pos] - (gq[1, 0] - gq[0, 1])) < 1e-12
         pos += 1
+
+
+def test_rht_one_hot_marginals_diagnostic():
+    # [RHT]: composing randomized Hadamard transforms makes the coordinates of
+    # any input close to Gaussian.  For the one-hot rows of the d = 8192, k = 3
+    # workload, sqrt(d) * y / ||y|| is exactly two-point (+-1) after one RHT,
+    # and its pooled per-coordinate marginal after two and three RHTs is
+    # compared with N(0, 1) by the Kolmogorov distance (a diagnostic; the bound
+    # below only guards against a broken transform: the values sit on a
+    # lattice of spacing 2 / sqrt(d), which alone keeps the distance near
+    # 0.2 * 2 / sqrt(d) ~ 0.004).
+    import scipy.stats
+    from structured_rotations_amd import workloads as W
+    w = W.make("rht3_8192_bf16", rows=256)
+    x = w["x"].astype(np.float64)
+    d = w["d"]
+    one_hot = x[(np.count_nonzero(x, axis=1) == 1)][:16]
+    assert one_hot.shape[0] >= 8
+    signs = w["signs"].astype(float)
+    dist = {}
+    for k in (1, 2, 3):
+        y = O.rht_compose(one_hot, signs[:k])
+        z = np.sqrt(d) * y / np.linalg.norm(y, axis=1, keepdims=True)
+        if k == 1:
+            np.testing.assert_allclose(np.abs(z), 1.0, atol=1e-12)
+            continue
+        dist[k] = scipy.stats.kstest(z.ravel(), "norm").statistic
+    print(f"Kolmogorov distance to N(0,1): k=2 {dist[2]:.4f}, k=3 {dist[3]:.4f}")
+    assert dist[2] < 0.02 and dist[3] < 0.02
