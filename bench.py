@@ -113,7 +113,7 @@ def cpu_baseline(w: dict, blk: str, budget_s: float = 30.0) -> dict:
                 "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread"}
 
 
-LAT_ROWS = (1, 2, 4, 8, 16, 32, 64)
+LAT_ROWS = (1, 2, 4, 8, 16, 32, 64, 128)
 
 
 def latency_main(args) -> int:
@@ -206,7 +206,7 @@ def latency_main(args) -> int:
         "higher_is_better": False,
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded rows and parameters of the named workload, first 1-64 rows)",
+        "data": "synthetic (seeded rows and parameters of the named workload, first 1-128 rows)",
         "config": {"workload": name, "d": d, "schedule": list(sch), "io": io, "blocks": args.blk,
                    "kind": "apply-latency", "parallelism": "single GPU"},
         "coefficient_bytes_per_call": cbytes,

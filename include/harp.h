@@ -192,6 +192,8 @@ harp_status harp_apply_inverse(const harp_schedule* s, int64_t d,
  * The digits are split into two runs and each run is one launch of many
  * small workgroups; fp32 rows are handed from the first launch to the second
  * through `workspace`, so the arithmetic is fp32 throughout as in harp_apply.
+ * Above 128 rows the call runs harp_apply's row kernels instead (faster at
+ * those sizes); the workspace is then left untouched.
  * harp_apply_decode_workspace() gives the bytes needed (rows * d * 4, or 0
  * when the whole row fits one workgroup and a single launch is made), or -1
  * if no split of the schedule fits (then harp_apply_decode returns

@@ -62,6 +62,7 @@ struct DecParams {
 };
 
 constexpr int kDecThreads = 256;
+constexpr int64_t kDecodeRowsMax = 128;   // more rows go to the throughput row kernels
 constexpr int kDecBatch = 16;    // loads in flight per thread
 
 __device__ __forceinline__ int sub_pos(const DecParams& p, int n, int h) {
@@ -591,7 +592,7 @@ hipError_t launch_one(const Plan& pl, const Run& run, bool inverse, bool first, 
                       const void* blocks, DT bdt, const float* scales, const int8_t* signs,
                       const void* x, int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt,
                       int64_t rows, hipStream_t stream) {
-  if (rows <= 64 && (run.t0 == 0 || run.t1 == pl.m)) {
+  if (run.t0 == 0 || run.t1 == pl.m) {
     bool done = false;
     hipError_t e = launch_fixed(pl, run, inverse, first, last, blocks, bdt, scales, signs, x, ldx, in_dt, y, ldy,
                                 out_dt, rows, stream, &done);
@@ -691,6 +692,11 @@ hipError_t launch_apply_decode(const Plan& pl, bool inverse, const void* blocks,
                                const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
                                int64_t rows, float* ws, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  // Above this many rows the 8-row tiles of the throughput kernels, which
+  // fetch every block once per tile rather than once per row block and run,
+  // are faster (measured crossover between 64 and 256 rows at d = 4096/5120).
+  if (rows > kDecodeRowsMax)
+    return launch_apply_rows(pl, inverse, blocks, bdt, scales, signs, x, ldx, io, y, ldy, io, rows, stream);
   Run runs[2];
   const int n = plan_runs(pl, bdt, runs);
   if (n == 0) return hipErrorInvalidValue;

@@ -71,8 +71,8 @@ def test_decode_other_schedules(sch, d, blk):
     assert_rows_close(from_dev(xr), O.apply_inverse(from_dev(y), sch, blocks_o, s), TOL["f32"], f"{sch} inverse")
 
 
-def test_decode_max_rows_and_sub_problem_chunks():
-    # 1024 rows: several sub-problems per workgroup in both digit runs.
+def test_decode_max_rows_hands_over_to_row_kernels():
+    # 1024 rows: above 128 rows the call runs the throughput row kernels.
     w = _case("cayley4096_bf16", 1024)
     sch, d = w["schedule"], w["d"]
     blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "bf16")
@@ -81,6 +81,23 @@ def test_decode_max_rows_and_sub_problem_chunks():
     blocks_o = oracle_blocks(sch, d, w["theta"], w["gauss"], "bf16")
     y_ref = O.apply(w["x"].astype(np.float64), sch, blocks_o, w["signs"].astype(float))
     assert_rows_close(from_dev(y), y_ref, TOL["bf16"], "1024 rows")
+
+
+def test_decode_sub_problem_chunks():
+    # 128 rows of a (4,4,4,4,4) schedule: no compile-time kernel for its runs,
+    # and the generic kernel puts two sub-problems in each workgroup.
+    sch, d = (4, 4, 4, 4, 4), 1024
+    print(f"\n[case] decode {sch} rows=128", flush=True)
+    g_sign, g_theta, _, g_data = I.streams(I.BASE_SEED + 400)
+    theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
+    signs = I.rademacher(g_sign, d)
+    x = g_data.standard_normal((128, d)).astype(np.float32)
+    blocks_g, _ = gpu_blocks(api, sch, d, theta, None, "f32")
+    y = api.harp_apply_decode(sch, d, blocks_g, None, signs_dev(signs), to_dev(x, "f32"))
+    torch.cuda.synchronize()
+    blocks_o = oracle_blocks(sch, d, theta, None, "f32")
+    y_ref = O.apply(x.astype(np.float64), sch, blocks_o, signs.astype(float))
+    assert_rows_close(from_dev(y), y_ref, TOL["f32"], "128 rows, two sub-problems per workgroup")
 
 
 def test_decode_in_place_strided_workspace_and_errors():
