@@ -1,0 +1,78 @@
+"""Seeded sweep over schedules, row counts, dtypes and entry points against the
+fp64 oracle (a wider net than the per-feature tests: radices 2..16 in random
+orders, every block format, with and without signs, both directions)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import harp_oracle as O
+from structured_rotations_amd import api
+from structured_rotations_amd import inputs as I
+from tests.parity_util import (TOL, assert_rows_close, from_dev, gpu_blocks, oracle_blocks, signs_dev, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+RADICES = (2, 3, 4, 5, 6, 7, 8, 9, 12, 16)
+
+
+def _cases(n, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = [((8, 8, 8), 512), ((4, 8, 4, 4), 512), ((2, 8, 8, 4), 512), ((8, 8, 4, 4, 2), 2048)]
+    while len(out) < n:
+        m = int(rng.integers(1, 6))
+        sch = tuple(int(b) for b in rng.choice(RADICES, m))
+        d = int(np.prod(sch))
+        if 2 <= d <= 4096 and (sch, d) not in out:
+            out.append((sch, d))
+    return out
+
+
+CASES = _cases(28)
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)))
+def test_sweep(idx):
+    sch, d = CASES[idx]
+    rng = np.random.default_rng(1000 + idx)
+    rows = int(rng.choice([1, 3, 9, 17, 33]))
+    io = ["f32", "bf16"][idx % 2]
+    blk = ["f32", "bf16", "i8"][idx % 3]
+    use_signs = idx % 4 != 3
+    print(f"\n[case] sweep {idx}: schedule {sch} d={d} rows={rows} io={io} blocks={blk} signs={use_signs}",
+          flush=True)
+    g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 500 + idx)
+    theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
+    gauss = I.gauss_mats(g_gauss, sch)
+    signs = I.rademacher(g_sign, d) if use_signs else None
+    x = g_data.standard_normal((rows, d)).astype(np.float32)
+    if io == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    blocks_g, scales_g = gpu_blocks(api, sch, d, theta, gauss, blk)
+    blocks_o = oracle_blocks(sch, d, theta, gauss, blk)
+    sg = signs_dev(signs) if use_signs else None
+    s = signs.astype(float) if use_signs else None
+    xd = to_dev(x, io)
+    y = api.harp_apply(sch, d, blocks_g, scales_g, sg, xd)
+    yd = api.harp_apply_decode(sch, d, blocks_g, scales_g, sg, xd)
+    torch.cuda.synchronize()
+    y_ref = O.apply(x.astype(np.float64), sch, blocks_o, s)
+    assert_rows_close(from_dev(y), y_ref, TOL[io], "harp_apply")
+    assert_rows_close(from_dev(yd), y_ref, TOL[io], "harp_apply_decode")
+    yin = from_dev(y)
+    xi = api.harp_apply_inverse(sch, d, blocks_g, scales_g, sg, y)
+    xid = api.harp_apply_decode(sch, d, blocks_g, scales_g, sg, y, inverse=True)
+    torch.cuda.synchronize()
+    x_ref = O.apply_inverse(yin, sch, blocks_o, s)
+    assert_rows_close(from_dev(xi), x_ref, TOL[io], "harp_apply_inverse")
+    assert_rows_close(from_dev(xid), x_ref, TOL[io], "harp_apply_decode inverse")
+    if max(sch) <= 8:
+        dy = np.random.default_rng(idx).standard_normal((rows, d)).astype(np.float32)
+        if io == "bf16":
+            dy = torch.from_numpy(dy).to(torch.bfloat16).float().numpy()
+        dx, db = api.harp_apply_vjp(sch, d, blocks_g, scales_g, sg, xd, to_dev(dy, io))
+        torch.cuda.synchronize()
+        rdx, rdb = O.apply_vjp(x.astype(np.float64), sch, blocks_o, s, dy.astype(np.float64))
+        assert_rows_close(from_dev(dx), rdx, TOL[io], "vjp dx")
+        ref = np.concatenate([b.ravel() for b in rdb])
+        got = db.cpu().numpy().astype(np.float64)
+        assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref), "vjp dB"
