@@ -76,3 +76,58 @@ def test_sweep(idx):
         ref = np.concatenate([b.ravel() for b in rdb])
         got = db.cpu().numpy().astype(np.float64)
         assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref), "vjp dB"
+
+
+TWO_SIDED = [((2, 3), (5, 2)), ((4, 4), (8,)), ((3, 3, 2), (2, 5, 4)), ((8, 2), (3, 7)), ((16,), (6, 2)),
+             ((5,), (4, 4, 4))]
+
+
+@pytest.mark.parametrize("idx", range(len(TWO_SIDED)))
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_sweep_two_sided(idx, use_ws):
+    su, sv = TWO_SIDED[idx]
+    du, dv = int(np.prod(su)), int(np.prod(sv))
+    io = ["f32", "bf16"][idx % 2]
+    print(f"\n[case] two-sided sweep {idx}: U {su} V {sv} io={io} workspace={use_ws}", flush=True)
+    g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 600 + idx)
+    tu, tv = I.theta_params(g_theta, su, du, 0.05, 0.1), I.theta_params(g_theta, sv, dv, 0.05, 0.1)
+    gu, gv = I.gauss_mats(g_gauss, su), I.gauss_mats(g_gauss, sv)
+    s_u, s_v = I.rademacher(g_sign, du), I.rademacher(g_sign, dv)
+    w = g_data.standard_normal((du, dv)).astype(np.float32)
+    if io == "bf16":
+        w = torch.from_numpy(w).to(torch.bfloat16).float().numpy()
+    bu, _ = gpu_blocks(api, su, du, tu, gu, "f32")
+    bv, _ = gpu_blocks(api, sv, dv, tv, gv, "f32")
+    ws = None
+    if use_ws:
+        ws = torch.empty(api.harp_rotate_weight_workspace(du, dv), dtype=torch.uint8, device="cuda")
+    wt = api.harp_rotate_weight(su, bu, None, signs_dev(s_u), sv, bv, None, signs_dev(s_v), to_dev(w, io),
+                                workspace=ws)
+    torch.cuda.synchronize()
+    obu, obv = oracle_blocks(su, du, tu, gu, "f32"), oracle_blocks(sv, dv, tv, gv, "f32")
+    ref = O.rotate_weight(w.astype(np.float64), su, obu, s_u.astype(float), sv, obv, s_v.astype(float))
+    # bf16 without a workspace rounds between the passes (three roundings)
+    tol = TOL[io] if (io == "f32" or use_ws) else TOL["bf16"]
+    got = from_dev(wt)
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= tol, f"relative Frobenius error {err:.3e}"
+
+
+RHT = [((2, 2, 2), 8, 1), ((4, 16), 64, 2), ((8, 8, 8), 512, 3), ((16, 2, 8), 256, 5)]
+
+
+@pytest.mark.parametrize("idx", range(len(RHT)))
+@pytest.mark.parametrize("inverse", [False, True])
+def test_sweep_rht(idx, inverse):
+    sch, d, k = RHT[idx]
+    io = ["f32", "bf16"][idx % 2]
+    print(f"\n[case] rht sweep {idx}: {sch} k={k} io={io} inverse={inverse}", flush=True)
+    g_sign, _, _, g_data = I.streams(I.BASE_SEED + 700 + idx)
+    signs = I.rademacher(g_sign, d, k=k)
+    x = g_data.standard_normal((13, d)).astype(np.float32)
+    if io == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    y = api.rht_compose(sch, d, signs_dev(signs), to_dev(x, io), inverse=inverse)
+    torch.cuda.synchronize()
+    ref = O.rht_compose(x.astype(np.float64), np.asarray(signs, dtype=float).reshape(k, d), inverse=inverse)
+    assert_rows_close(from_dev(y), ref, TOL[io], "rht_compose")
