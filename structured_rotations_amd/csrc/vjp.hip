@@ -10,8 +10,9 @@
 //   dL/dx = D_s g_0.
 // The forward launches store x_1 .. x_{m-1} (fp32) in the workspace; x_0 is
 // re-read from x.  Each backward launch handles one stage: a thread owns one
-// group and a chunk of rows, keeps the group's block and its b x b gradient
-// in registers, and writes the gradient of its chunk to a slot of its own;
+// group (half a group for radices 6..8) and a chunk of rows, keeps its part
+// of the group's block and of its b x b gradient in registers, and writes the
+// gradient of its chunk to a slot of its own;
 // a last launch sums the slots in a fixed order (no atomics, so the result
 // does not depend on scheduling).  Radices up to 8.
 #include "common.h"
@@ -53,16 +54,6 @@ struct VjpArgs {
   int64_t n_blk;
 };
 
-__device__ __forceinline__ float ld_any(const void* p, int64_t i, int bf) {
-  return bf ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
-}
-__device__ __forceinline__ void st_any(void* p, int64_t i, int bf, float v) {
-  if (bf)
-    static_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_rne(v);
-  else
-    static_cast<float*>(p)[i] = v;
-}
-
 template <typename TB>
 __device__ __forceinline__ float coef_at(const TB* b, int64_t i);
 template <>
@@ -82,8 +73,16 @@ __device__ __forceinline__ void load_block(const VjpArgs& a, int c, float (&blk)
     for (int k = 0; k < B; ++k) blk[r][k] = coef_at<TB>(bp, r * B + k) * sc;
 }
 
-// x_{t+1} = S_t x_t for the rows of one chunk and one group.
-template <int B, typename TB>
+// x_{t+1} = S_t x_t for the rows of one chunk and one group (TX: bf16 only
+// when the input is the caller's x, t = 0).
+template <typename T>
+__device__ __forceinline__ float ld_t(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_t<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_t<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <int B, typename TB, typename TX>
 __global__ void __launch_bounds__(kVjpThreads) vjp_fwd_kernel(VjpArgs a) {
   const int64_t id = (int64_t)blockIdx.x * kVjpThreads + threadIdx.x;
   if (id >= (int64_t)a.st.ngroups * a.nchunk) return;
@@ -98,70 +97,126 @@ __global__ void __launch_bounds__(kVjpThreads) vjp_fwd_kernel(VjpArgs a) {
   for (int j = 0; j < B; ++j) sg[j] = a.x_sign ? (float)a.signs[base + j * s] : 1.0f;
   const int64_t r0 = (int64_t)chunk * a.rpc;
   const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
+  const TX* xin = static_cast<const TX*>(a.xin) + base;
+  float* out = static_cast<float*>(a.out) + base;
   for (int64_t row = r0; row < r1; ++row) {
+    const TX* xr = xin + row * a.ldx;
+    float* orow = out + row * a.ldo;
     float v[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) v[j] = ld_any(a.xin, row * a.ldx + base + j * s, a.x_bf16) * sg[j];
+    for (int j = 0; j < B; ++j) v[j] = ld_t<TX>(xr, j * s) * sg[j];
 #pragma unroll
     for (int r = 0; r < B; ++r) {
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < B; ++k) acc = fmaf(blk[r][k], v[k], acc);
-      static_cast<float*>(a.out)[row * a.ldo + base + r * s] = acc;
+      orow[r * s] = acc;
     }
   }
 }
 
-// g_t = S_t^T g_{t+1} and the chunk's sum of g_{t+1}[c] x_t[c]^T.
-template <int B, typename TB>
+// Threads per group in the backward launch: radices 6..8 split a group over
+// two threads (thread h owns gradient rows and block columns [h*RH, h*RH+RH)),
+// which halves the registers a thread keeps and doubles the waves per SIMD.
+template <int B>
+constexpr int bwd_split() {
+  return B >= 6 ? 2 : 1;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_t(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st_t<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void st_t<uint16_t>(uint16_t* p, int64_t i, float v) {
+  p[i] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+// g_t = S_t^T g_{t+1} and the chunk's sum of g_{t+1}[c] x_t[c]^T.  TX, TG, TO:
+// element types of x_t, g_{t+1} and the output (bf16 only where they are the
+// caller's rows: x and dx for t = 0, dy for t = m - 1).
+template <int B, typename TB, typename TX, typename TG, typename TO>
 __global__ void __launch_bounds__(kVjpThreads) vjp_bwd_kernel(VjpArgs a) {
+  constexpr int H = bwd_split<B>();
+  constexpr int RH = (B + H - 1) / H;            // rows (and columns) per thread
   const int64_t id = (int64_t)blockIdx.x * kVjpThreads + threadIdx.x;
-  if (id >= (int64_t)a.st.ngroups * a.nchunk) return;
-  const int c = (int)(id % a.st.ngroups);
-  const int chunk = (int)(id / a.st.ngroups);
+  if (id >= (int64_t)a.st.ngroups * a.nchunk * H) return;
+  const int h = (int)(id % H);
+  const int64_t gid = id / H;
+  const int c = (int)(gid % a.st.ngroups);
+  const int chunk = (int)(gid / a.st.ngroups);
   const int s = a.st.s;
   const int64_t base = (int64_t)(c / s) * B * s + c % s;
-  float blk[B][B];
-  load_block<B, TB>(a, c, blk);
-  float xs[B], os[B];
-#pragma unroll
-  for (int j = 0; j < B; ++j) {
-    xs[j] = a.x_sign ? (float)a.signs[base + j * s] : 1.0f;
-    os[j] = a.o_sign ? (float)a.signs[base + j * s] : 1.0f;
-  }
-  float acc[B][B];
-#pragma unroll
-  for (int r = 0; r < B; ++r)
-#pragma unroll
-    for (int k = 0; k < B; ++k) acc[r][k] = 0.0f;
-  const int64_t r0 = (int64_t)chunk * a.rpc;
-  const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
-  for (int64_t row = r0; row < r1; ++row) {
-    float g[B], v[B];
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      g[j] = ld_any(a.gin, row * a.ldg + base + j * s, a.g_bf16);
-      v[j] = ld_any(a.xin, row * a.ldx + base + j * s, a.x_bf16) * xs[j];
-    }
+  // blk[r][kk] = B[r][h * RH + kk]: the block columns this thread's outputs need
+  float blk[B][RH];
+  {
+    const TB* bp = static_cast<const TB*>(a.blocks) + a.st.blk_off + (int64_t)c * B * B;
+    const float sc = sizeof(TB) == 1 ? a.scales[a.st.grp_off + c] : 1.0f;
 #pragma unroll
     for (int r = 0; r < B; ++r)
 #pragma unroll
-      for (int k = 0; k < B; ++k) acc[r][k] = fmaf(g[r], v[k], acc[r][k]);
+      for (int kk = 0; kk < RH; ++kk) {
+        const int k = h * RH + kk;
+        blk[r][kk] = k < B ? coef_at<TB>(bp, r * B + k) * sc : 0.0f;
+      }
+  }
+  float xs[B], os[RH];
+#pragma unroll
+  for (int j = 0; j < B; ++j) xs[j] = a.x_sign ? (float)a.signs[base + j * s] : 1.0f;
+#pragma unroll
+  for (int kk = 0; kk < RH; ++kk) {
+    const int k = h * RH + kk;
+    os[kk] = (a.o_sign && k < B) ? (float)a.signs[base + k * s] : 1.0f;
+  }
+  float acc[RH][B];
+#pragma unroll
+  for (int rr = 0; rr < RH; ++rr)
+#pragma unroll
+    for (int k = 0; k < B; ++k) acc[rr][k] = 0.0f;
+  const int64_t r0 = (int64_t)chunk * a.rpc;
+  const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
+  const TG* gin = static_cast<const TG*>(a.gin) + base;
+  const TX* xin = static_cast<const TX*>(a.xin) + base;
+  TO* out = static_cast<TO*>(a.out) + base;
+  for (int64_t row = r0; row < r1; ++row) {
+    const TG* gr = gin + row * a.ldg;
+    const TX* xr = xin + row * a.ldx;
+    float g[B], v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      g[j] = ld_t<TG>(gr, j * s);
+      v[j] = ld_t<TX>(xr, j * s) * xs[j];
+    }
+#pragma unroll
+    for (int rr = 0; rr < RH; ++rr) {
+      const int r = h * RH + rr;
+      const float gv = r < B ? g[r < B ? r : 0] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < B; ++k) acc[rr][k] = fmaf(gv, v[k], acc[rr][k]);
+    }
     if (a.out != nullptr) {
+      TO* orow = out + row * a.ldo;
 #pragma unroll
-      for (int k = 0; k < B; ++k) {
-        float o = 0.0f;
+      for (int kk = 0; kk < RH; ++kk) {
+        const int k = h * RH + kk;
+        if (k < B) {
+          float o = 0.0f;
 #pragma unroll
-        for (int r = 0; r < B; ++r) o = fmaf(blk[r][k], g[r], o);
-        st_any(a.out, row * a.ldo + base + k * s, a.o_bf16, o * os[k]);
+          for (int r = 0; r < B; ++r) o = fmaf(blk[r][kk], g[r], o);
+          st_t<TO>(orow, k * s, o * os[kk]);
+        }
       }
     }
   }
   float* pp = a.partial + (int64_t)chunk * a.n_blk + a.st.blk_off + (int64_t)c * B * B;
 #pragma unroll
-  for (int r = 0; r < B; ++r)
+  for (int rr = 0; rr < RH; ++rr) {
+    const int r = h * RH + rr;
+    if (r < B) {
 #pragma unroll
-    for (int k = 0; k < B; ++k) pp[r * B + k] = acc[r][k];
+      for (int k = 0; k < B; ++k) pp[r * B + k] = acc[rr][k];
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kVjpThreads) vjp_reduce_kernel(const float* partial, int nchunk, int64_t n_blk,
@@ -185,12 +240,27 @@ int vjp_chunks(const Plan& pl, int64_t rows) {
 
 template <int B, typename TB>
 hipError_t launch_stage(bool fwd, const VjpArgs& a, hipStream_t st) {
-  const int64_t n = (int64_t)a.st.ngroups * a.nchunk;
+  const int64_t n = (int64_t)a.st.ngroups * a.nchunk * (fwd ? 1 : bwd_split<B>());
   const int64_t grid = (n + kVjpThreads - 1) / kVjpThreads;
-  if (fwd)
-    hipLaunchKernelGGL((vjp_fwd_kernel<B, TB>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((vjp_bwd_kernel<B, TB>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a);
+  if (fwd) {
+    if (a.x_bf16)
+      hipLaunchKernelGGL((vjp_fwd_kernel<B, TB, uint16_t>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((vjp_fwd_kernel<B, TB, float>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a);
+  } else {
+    using F = float;
+    using H16 = uint16_t;
+    const int code = (a.x_bf16 ? 4 : 0) | (a.g_bf16 ? 2 : 0) | (a.o_bf16 ? 1 : 0);
+    switch (code) {
+      case 0: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, F, F, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      case 5: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, F, H16>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, F, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, F, H16, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      case 7: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, H16, H16>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      case 6: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, H16, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
