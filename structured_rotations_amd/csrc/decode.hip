@@ -583,6 +583,7 @@ hipError_t launch_fixed(const Plan& pl, const Run& run, bool inverse, bool first
   if (run_is<8, 8>(pl, run)) e = launch_fixed_io<RunT<8, 8>>(in_dt, out_dt, bdt, p, (int)grid, stream);
   else if (run_is<8, 5, 2>(pl, run)) e = launch_fixed_io<RunT<8, 5, 2>>(in_dt, out_dt, bdt, p, (int)grid, stream);
   else if (run_is<8, 3, 3, 3>(pl, run)) e = launch_fixed_io<RunT<8, 3, 3, 3>>(in_dt, out_dt, bdt, p, (int)grid, stream);
+  else if (run_is<8, 16>(pl, run)) e = launch_fixed_io<RunT<8, 16>>(in_dt, out_dt, bdt, p, (int)grid, stream);
   else return hipSuccess;
   *done = true;
   return e;

@@ -45,7 +45,7 @@ def test_decode_matches_oracle(name, blk, rows):
 
 
 OTHER = [((8, 8, 8, 3, 3, 3), 13824), ((3, 7, 16, 2), 672), ((16, 16, 16), 4096), ((2, 5, 4), 40),
-         ((4, 4, 4, 4, 4), 1024)]
+         ((4, 4, 4, 4, 4), 1024), ((8, 8, 8, 16), 8192)]
 
 
 @pytest.mark.parametrize("sch,d", OTHER)
