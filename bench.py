@@ -46,6 +46,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 (vector and matrix)
 
 
 def kernel_hash(kernel: str) -> str:
@@ -414,6 +415,7 @@ def main() -> int:
         def step():
             y.copy_(x)
         alg_bytes = rows * d * eb * 2
+        alg_flops = 0
         units = rows
     elif wl.kind == "rht":
         sg = torch.from_numpy(w["signs"]).cuda()
@@ -421,6 +423,8 @@ def main() -> int:
         def step():
             api.rht_compose(sch, d, sg, x, y)
         alg_bytes = rows * d * eb * 2
+        # k fast Walsh-Hadamard transforms: d log2 d add/sub each, plus the scale
+        alg_flops = rows * w["k"] * d * (int(np.log2(d)) + 1)
         units = rows
     elif wl.kind == "two_sided":
         bu, scu = api.harp_materialize_blocks(w["su"], w["d_out"], torch.from_numpy(w["theta_u"]).cuda(),
@@ -433,6 +437,8 @@ def main() -> int:
         def step():
             api.harp_rotate_weight(w["su"], bu, scu, su_s, sch, bv, scv, sv_s, x, y)
         alg_bytes = rows * d * eb * 2
+        # b_t FMAs per element per stage, both sides
+        alg_flops = 2 * rows * d * (sum(sch) + sum(w["su"]))
         units = 1
     else:
         th = torch.from_numpy(w["theta"]).cuda()
@@ -443,6 +449,7 @@ def main() -> int:
         def step():
             api.harp_apply(sch, d, blocks, scales, sg, x, y)
         alg_bytes = rows * d * eb * 2
+        alg_flops = 2 * rows * d * sum(sch)      # b_t FMAs per element per stage
         units = rows
     torch.cuda.synchronize()
 
@@ -518,6 +525,10 @@ def main() -> int:
         "kernel_ms_p10_p90": [round(float(np.percentile(per_launch, 10)), 5),
                               round(float(np.percentile(per_launch, 90)), 5)],
         "alg_bytes_per_launch": alg_bytes,
+        "compute": {"alg_flops_per_launch": alg_flops,
+                    "achieved_tflops": round(alg_flops / (kern_ms * 1e-3) / 1e12, 2),
+                    "peak_tflops_fp32": FP32_PEAK_TFLOPS,
+                    "frac": round(alg_flops / (kern_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4)},
         "kernel_ms_mean_flushed": None if flushed is None else round(float(flushed.mean()), 5),
         "wall_s_timed": round(wall, 4),
         "parity_max_row_rel_l2": parity,

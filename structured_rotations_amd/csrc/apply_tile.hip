@@ -235,15 +235,20 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
   // (one workgroup per CU), small rows leave room for several workgroups.
   const size_t row_bytes = (size_t)p.ldsrow * sizeof(float);
   const size_t budget = pl.d >= 2048 ? (size_t)160 * 1024 : (size_t)64 * 1024;
+  const int threads = pl.d >= 2048 ? 512 : 256;
+  const int wg_per_cu = pl.d >= 2048 ? 1 : 2;
+  const int64_t slots = (int64_t)device_cu_count() * wg_per_cu;
   int64_t R = (int64_t)(budget / row_bytes);
   if (R < 1) R = 1;
+  // a small batch is spread over every workgroup slot rather than packed
+  // into as few tiles as the LDS allows
+  const int64_t spread = (rows + slots - 1) / slots;
+  if (R > spread) R = spread;
   if (R > rows) R = rows;
   p.R = (int)R;
   p.ntiles = (rows + R - 1) / R;
   const size_t lds = (size_t)R * row_bytes;
-  const int threads = pl.d >= 2048 ? 512 : 256;
-  const int wg_per_cu = pl.d >= 2048 ? 1 : 2;
-  int64_t grid = (int64_t)device_cu_count() * wg_per_cu;
+  int64_t grid = slots;
   if (grid > p.ntiles) grid = p.ntiles;
   if (in_dt == DT::F32 && out_dt == DT::F32) return launch_blk<float, float>(bdt, p, threads, (int)grid, lds, stream);
   if (in_dt == DT::BF16 && out_dt == DT::BF16) return launch_blk<uint16_t, uint16_t>(bdt, p, threads, (int)grid, lds, stream);
