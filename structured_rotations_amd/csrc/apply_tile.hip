@@ -97,7 +97,10 @@ __device__ void stage_impl(const TileParams& p, const StageDesc& sd, float* tile
   }
 }
 
-template <typename TB>
+// BIG: radices 9..16 compiled in.  Their b x b register blocks set the
+// register count (and spills) of the whole kernel, so schedules whose radices
+// are all at most 8 run a variant without them.
+template <typename TB, bool BIG>
 __device__ void run_stage(const TileParams& p, int t, float* tile, int nr) {
   const StageDesc& sd = p.st[t];
   switch (sd.b) {
@@ -108,19 +111,25 @@ __device__ void run_stage(const TileParams& p, int t, float* tile, int nr) {
     case 6: stage_impl<6, TB>(p, sd, tile, nr); break;
     case 7: stage_impl<7, TB>(p, sd, tile, nr); break;
     case 8: stage_impl<8, TB>(p, sd, tile, nr); break;
-    case 9: stage_impl<9, TB>(p, sd, tile, nr); break;
-    case 10: stage_impl<10, TB>(p, sd, tile, nr); break;
-    case 11: stage_impl<11, TB>(p, sd, tile, nr); break;
-    case 12: stage_impl<12, TB>(p, sd, tile, nr); break;
-    case 13: stage_impl<13, TB>(p, sd, tile, nr); break;
-    case 14: stage_impl<14, TB>(p, sd, tile, nr); break;
-    case 15: stage_impl<15, TB>(p, sd, tile, nr); break;
-    case 16: stage_impl<16, TB>(p, sd, tile, nr); break;
-    default: break;
+    default:
+      if constexpr (BIG) {
+        switch (sd.b) {
+          case 9: stage_impl<9, TB>(p, sd, tile, nr); break;
+          case 10: stage_impl<10, TB>(p, sd, tile, nr); break;
+          case 11: stage_impl<11, TB>(p, sd, tile, nr); break;
+          case 12: stage_impl<12, TB>(p, sd, tile, nr); break;
+          case 13: stage_impl<13, TB>(p, sd, tile, nr); break;
+          case 14: stage_impl<14, TB>(p, sd, tile, nr); break;
+          case 15: stage_impl<15, TB>(p, sd, tile, nr); break;
+          case 16: stage_impl<16, TB>(p, sd, tile, nr); break;
+          default: break;
+        }
+      }
+      break;
   }
 }
 
-template <typename TIN, typename TOUT, typename TB>
+template <typename TIN, typename TOUT, typename TB, bool BIG>
 __global__ void __launch_bounds__(512) apply_tile_kernel(TileParams p) {
   extern __shared__ float tile[];
   for (int64_t tix = blockIdx.x; tix < p.ntiles; tix += gridDim.x) {
@@ -130,7 +139,7 @@ __global__ void __launch_bounds__(512) apply_tile_kernel(TileParams p) {
     load_tile<TIN>(p, tile, row0, nr);
     __syncthreads();
     for (int t = 0; t < p.m; ++t) {
-      run_stage<TB>(p, t, tile, nr);
+      run_stage<TB, BIG>(p, t, tile, nr);
       __syncthreads();
     }
     store_tile<TOUT>(p, tile, row0, nr);
@@ -162,9 +171,9 @@ int device_cu_count() {
   return cus;
 }
 
-template <typename TIN, typename TOUT, typename TB>
+template <typename TIN, typename TOUT, typename TB, bool BIG>
 hipError_t launch_typed(const TileParams& p, int threads, int grid, size_t lds, hipStream_t stream) {
-  auto kern = apply_tile_kernel<TIN, TOUT, TB>;
+  auto kern = apply_tile_kernel<TIN, TOUT, TB, BIG>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -172,14 +181,22 @@ hipError_t launch_typed(const TileParams& p, int threads, int grid, size_t lds, 
   return hipGetLastError();
 }
 
-template <typename TIN, typename TOUT>
-hipError_t launch_blk(DT bdt, const TileParams& p, int threads, int grid, size_t lds, hipStream_t st) {
+template <typename TIN, typename TOUT, bool BIG>
+hipError_t launch_blk_b(DT bdt, const TileParams& p, int threads, int grid, size_t lds, hipStream_t st) {
   switch (bdt) {
-    case DT::F32: return launch_typed<TIN, TOUT, float>(p, threads, grid, lds, st);
-    case DT::BF16: return launch_typed<TIN, TOUT, uint16_t>(p, threads, grid, lds, st);
-    case DT::I8: return launch_typed<TIN, TOUT, int8_t>(p, threads, grid, lds, st);
+    case DT::F32: return launch_typed<TIN, TOUT, float, BIG>(p, threads, grid, lds, st);
+    case DT::BF16: return launch_typed<TIN, TOUT, uint16_t, BIG>(p, threads, grid, lds, st);
+    case DT::I8: return launch_typed<TIN, TOUT, int8_t, BIG>(p, threads, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename TIN, typename TOUT>
+hipError_t launch_blk(DT bdt, const TileParams& p, int threads, int grid, size_t lds, hipStream_t st) {
+  bool big = false;
+  for (int i = 0; i < p.m; ++i) big = big || p.st[i].b > 8;
+  return big ? launch_blk_b<TIN, TOUT, true>(bdt, p, threads, grid, lds, st)
+             : launch_blk_b<TIN, TOUT, false>(bdt, p, threads, grid, lds, st);
 }
 
 }  // namespace
