@@ -84,7 +84,8 @@ template <typename T>
 __device__ __forceinline__ u32x4 pack_row(const float* v);
 template <>
 __device__ __forceinline__ u32x4 pack_row<uint16_t>(const float* v) {
-  return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  return u32x4{pack_bf16x2_hw(v[0], v[1]), pack_bf16x2_hw(v[2], v[3]), pack_bf16x2_hw(v[4], v[5]),
+               pack_bf16x2_hw(v[6], v[7])};
 }
 template <>
 __device__ __forceinline__ u32x4 pack_row<float>(const float* v) {

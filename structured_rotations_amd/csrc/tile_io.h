@@ -54,8 +54,8 @@ __device__ __forceinline__ u32x4 pack16(const float* v);
 template <>
 __device__ __forceinline__ u32x4 pack16<uint16_t>(const float* v) {
   u32x4 w;
-  w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
-  w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
+  w.x = pack_bf16x2_hw(v[0], v[1]); w.y = pack_bf16x2_hw(v[2], v[3]);
+  w.z = pack_bf16x2_hw(v[4], v[5]); w.w = pack_bf16x2_hw(v[6], v[7]);
   return w;
 }
 template <>
