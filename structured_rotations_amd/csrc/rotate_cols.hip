@@ -86,53 +86,50 @@ __device__ __forceinline__ ColTile col_tile(const ColParams& p, int64_t tix) {
   return t;
 }
 
-// Coefficients of one stage of one tile, fp32 C[o][k] (C = B forward, B^T
-// inverse; int8 blocks dequantised), with the signs folded in: the first
-// stage of a run with sign_mode 1 takes C[o][k] * s(row of input k), the last
-// one with sign_mode 2 takes s(row of output o) * C[o][k] -- the same
-// products as flipping the tile rows before or after, without touching the
-// data.  Thread t fetches elements e = t + u * 512 of the ngl * b * b (later
-// elements repeat the last one), NCU of them, into registers one stage ahead.
+// Coefficients of one stage of one tile, C[o][k] (C = B forward, B^T
+// inverse), fetched into registers a stage ahead as the stored words (fp32
+// bits, bf16 bits, or int8 code and its fp32 scale); coef_put turns them into
+// fp32.  Thread t fetches elements e = t + u * 512 of the ngl * b * b, NCU of
+// them; slots past the stage's count repeat its last element.  Every thread
+// issues exactly NCU loads (2 NCU for int8) and nothing is computed from them
+// before coef_put, so the wait in front of coef_put is for these loads and the
+// ones before them, never for the tile prefetch issued after them.
 template <typename TB, int NCU>
-__device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColTile& t, float (&cr)[NCU]) {
+__device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColTile& t, uint32_t (&cw)[NCU],
+                                           float (&csc)[NCU]) {
   const ColStage& cs = p.st[s];
   const int B = cs.b, BB = B * B, ngl = p.nsub / B;
   const int n = ngl * BB;
-  const int ncu = cs.ncu;   // slots this stage needs (n <= 512 * ncu)
   // group c = (pre * ngl + gl) * suf + q: uniform base plus gl * suf
   const TB* blocks = static_cast<const TB*>(p.blocks) + cs.blk_off +
                      (t.pre * (int64_t)ngl * p.suf + t.q) * BB;
   const float* scales = p.scales + cs.grp_off + t.pre * (int64_t)ngl * p.suf + t.q;
-  const int8_t* signs = p.signs + t.row_base;
-  const bool sin = p.sign_mode == 1 && s == 0;
-  const bool sout = p.sign_mode == 2 && s == p.nstage - 1;
   const int sufi = (int)p.suf;
 #pragma unroll
   for (int u = 0; u < NCU; ++u) {
-    if (u < ncu) {
-      int e = threadIdx.x + u * 512;
-      e = e < n ? e : n - 1;
-      const int gl = udiv(e, cs.mag_bb);
-      const int i = e - gl * BB;
-      const int o = udiv(i, cs.mag_b);
-      const int k = i - o * B;
-      float scale = 1.0f;
-      if constexpr (std::is_same<TB, int8_t>::value) scale = scales[gl * sufi];
-      float v = coef<TB>(blocks, gl * sufi * BB + (p.transpose ? k * B + o : i), scale);
-      if (sin || sout) {
-        const int hi = udiv(gl, cs.mag_ls);
-        const int u_row = hi * B * cs.ls + (gl - hi * cs.ls) + (sin ? k : o) * cs.ls;
-        if (signs[u_row * sufi] < 0) v = -v;
-      }
-      cr[u] = v;
+    int e = threadIdx.x + u * 512;
+    e = e < n ? e : n - 1;
+    const int gl = udiv(e, cs.mag_bb);
+    const int i = e - gl * BB;
+    const int o = udiv(i, cs.mag_b);
+    const int k = i - o * B;
+    const TB* src = blocks + gl * sufi * BB + (p.transpose ? k * B + o : i);
+    if constexpr (std::is_same<TB, float>::value) {
+      cw[u] = __float_as_uint(*src);
+    } else if constexpr (std::is_same<TB, uint16_t>::value) {
+      cw[u] = *src;
+    } else {
+      cw[u] = (uint32_t)(int)*src;
+      csc[u] = scales[gl * sufi];
     }
   }
 }
 
-// Writes the fetched coefficients into a slot as C[gl][o][k] with rows padded
-// to 4 floats (the layout the stage tasks read).
-template <int NCU>
-__device__ __forceinline__ void coef_put(const ColParams& p, int s, const float (&cr)[NCU], float* slot) {
+// Writes the fetched coefficients into a slot as C[gl][o][k] in fp32 with
+// rows padded to 4 floats (the layout the stage tasks read).
+template <typename TB, int NCU>
+__device__ __forceinline__ void coef_put(const ColParams& p, int s, const uint32_t (&cw)[NCU], const float (&csc)[NCU],
+                                         float* slot) {
   const ColStage& cs = p.st[s];
   const int B = cs.b, BB = B * B, Bp = (B + 3) & ~3;
   const int n = (p.nsub / B) * BB;
@@ -143,7 +140,11 @@ __device__ __forceinline__ void coef_put(const ColParams& p, int s, const float 
       const int gl = udiv(e, cs.mag_bb);
       const int i = e - gl * BB;
       const int o = udiv(i, cs.mag_b);
-      slot[gl * (B * Bp) + o * Bp + (i - o * B)] = cr[u];
+      float v;
+      if constexpr (std::is_same<TB, float>::value) v = __uint_as_float(cw[u]);
+      else if constexpr (std::is_same<TB, uint16_t>::value) v = __uint_as_float(cw[u] << 16);
+      else v = (float)(int)cw[u] * csc[u];
+      slot[gl * (B * Bp) + o * Bp + (i - o * B)] = v;
     }
   }
 }
@@ -305,8 +306,13 @@ __device__ __forceinline__ int chunk_of(int j, int total) {
   return i < total ? i : (total >= 512 ? (int)threadIdx.x : i % total);
 }
 
+// The D_s factor of the pass (sign_mode 1: on the rows as they enter the
+// first stage; 2: on the rows as they leave the last one) is applied to the
+// data chunks in the swap, from one sign byte per chunk slot loaded with the
+// chunk (a byte of the blocks when there are no signs: always a valid
+// address, never used).  Every thread issues the same 2 MAXC loads per tile.
 template <typename TIN, int MAXC>
-__device__ __forceinline__ void col_prefetch(const ColParams& p, const ColTile& t, u32x4 (&r)[MAXC]) {
+__device__ __forceinline__ void col_prefetch(const ColParams& p, const ColTile& t, u32x4 (&r)[MAXC], uint8_t (&sg)[MAXC]) {
   constexpr int VI = ColIo<TIN>::V;
   const TIN* x = static_cast<const TIN*>(p.x);
   const int cpr = p.pw / VI;
@@ -316,13 +322,23 @@ __device__ __forceinline__ void col_prefetch(const ColParams& p, const ColTile& 
     const int i = chunk_of(j, total);
     const int u = i / cpr;
     const int ch = i - u * cpr;
-    r[j] = ld_stream(x + (t.row_base + (int64_t)u * p.suf) * p.ldx + t.col0 + ch * VI);
+    const int64_t row = t.row_base + (int64_t)u * p.suf;
+    r[j] = ld_stream(x + row * p.ldx + t.col0 + ch * VI);
+    // the raw byte; its bit 7 is tested in the swap
+    sg[j] = reinterpret_cast<const uint8_t*>(p.signs)[p.sign_mode ? row : 0];
   }
 }
 
+// Sign bit(s) of every value of a 16-byte chunk
+template <typename T> struct ChunkSign;
+template <> struct ChunkSign<uint16_t> { static constexpr uint32_t m = 0x80008000u; };
+template <> struct ChunkSign<float> { static constexpr uint32_t m = 0x80000000u; };
+__device__ __forceinline__ u32x4 flip_chunk(u32x4 w, uint32_t m) { return u32x4{w.x ^ m, w.y ^ m, w.z ^ m, w.w ^ m}; }
+
 template <typename TIN, typename TOUT, int MAXC>
 __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile& done, bool has_done, bool has_next,
-                                              const u32x4 (&r)[MAXC], float* tile) {
+                                              const u32x4 (&r)[MAXC], const uint8_t (&sg)[MAXC], uint32_t& smask,
+                                              float* tile) {
   constexpr int V = ColIo<TIN>::V;
   static_assert(ColIo<TIN>::V == ColIo<TOUT>::V || true, "");
   constexpr int VI = ColIo<TIN>::V, VO = ColIo<TOUT>::V;
@@ -333,6 +349,7 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
   const int total = p.nsub * cpr_i;
   constexpr int NO = VI / VO > 0 ? VI / VO : 1;
   u32x4 keep[NO];   // slot 0's finished data, stored again by repeated slots
+  uint32_t nmask = 0;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
     const int i = chunk_of(j, total);
@@ -351,6 +368,7 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
           v[e] = q4.x; v[e + 1] = q4.y; v[e + 2] = q4.z; v[e + 3] = q4.w;
         }
         u32x4 o = pack_chunk(v, static_cast<TOUT*>(nullptr));
+        if (p.sign_mode == 2 && ((smask >> j) & 1u)) o = flip_chunk(o, ChunkSign<TOUT>::m);
         if (j == 0) keep[h] = o;
         else if (rep) o = keep[h];
         st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI + h * VO, o);
@@ -372,29 +390,37 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
       }
     }
     if (has_next) {
+      const bool neg = (sg[j] & 0x80) != 0;
+      nmask |= (neg ? 1u : 0u) << j;
       float v[VI];
-      unpack_chunk(r[j], v, static_cast<const TIN*>(nullptr));
+      unpack_chunk(p.sign_mode == 1 && neg ? flip_chunk(r[j], ChunkSign<TIN>::m) : r[j], v,
+                   static_cast<const TIN*>(nullptr));
 #pragma unroll
       for (int e = 0; e < VI; e += 4) *reinterpret_cast<f32x4*>(loc + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
     }
   }
+  if (has_next) smask = nmask;
 }
 
 // Slot by slot: store the finished tile's chunk (unless there is none yet),
 // then put the next tile's chunk in its place; the same thread owns both.
+// smask holds, per slot, whether the row of the tile in LDS has a negative
+// sign: it is the same row in every tile of the pass, and the swap replaces
+// it with the incoming tile's.
 // When slots wrap around to other threads' chunks (p.dup), a chunk has two
 // owners, and one of them could overwrite it before the other has stored it:
 // then every store is done first and a barrier separates them from the
 // writes.
 template <typename TIN, typename TOUT, int MAXC>
 __device__ __forceinline__ void col_swap(const ColParams& p, const ColTile& done, bool has_done, bool has_next,
-                                         const u32x4 (&r)[MAXC], float* tile) {
+                                         const u32x4 (&r)[MAXC], const uint8_t (&sg)[MAXC], uint32_t& smask,
+                                         float* tile) {
   if (p.dup) {
-    if (has_done) col_swap_part<TIN, TOUT, MAXC>(p, done, true, false, r, tile);
+    if (has_done) col_swap_part<TIN, TOUT, MAXC>(p, done, true, false, r, sg, smask, tile);
     __syncthreads();
-    if (has_next) col_swap_part<TIN, TOUT, MAXC>(p, done, false, true, r, tile);
+    if (has_next) col_swap_part<TIN, TOUT, MAXC>(p, done, false, true, r, sg, smask, tile);
   } else {
-    col_swap_part<TIN, TOUT, MAXC>(p, done, has_done, has_next, r, tile);
+    col_swap_part<TIN, TOUT, MAXC>(p, done, has_done, has_next, r, sg, smask, tile);
   }
 }
 
@@ -408,11 +434,16 @@ __device__ __forceinline__ void col_swap_el(const ColParams& p, const ColTile& d
   for (int i = threadIdx.x; i < p.nsub * p.pw; i += 512) {
     const int u = i / p.pw;
     const int j = i - u * p.pw;
-    if (has_done && j < done.w) st_el(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + j, tile[i]);
+    if (has_done && j < done.w) {
+      const int64_t row = done.row_base + (int64_t)u * p.suf;
+      const float v = tile[i];
+      st_el(y + row * p.ldy + done.col0 + j, p.sign_mode == 2 && p.signs[row] < 0 ? -v : v);
+    }
     if (has_next) {
       float v = 0.0f;
-      if (j < nt.w) v = ld_el(x + (nt.row_base + (int64_t)u * p.suf) * p.ldx + nt.col0 + j);
-      tile[i] = v;
+      const int64_t row = nt.row_base + (int64_t)u * p.suf;
+      if (j < nt.w) v = ld_el(x + row * p.ldx + nt.col0 + j);
+      tile[i] = p.sign_mode == 1 && p.signs[row] < 0 ? -v : v;
     }
   }
 }
@@ -424,7 +455,9 @@ __device__ __forceinline__ void col_swap_el(const ColParams& p, const ColTile& d
 // for the prefetched next one chunk by chunk after the last stage.  Every
 // thread issues the same global loads whatever the position in the pass
 // (past the last tile it re-reads the last one), so the waits count them
-// exactly and a stage never waits for the tile prefetch.
+// exactly: the prefetch is issued in the first stage behind that stage's
+// coefficient fetch, and only the last stage's coefficients (fetched behind
+// it) and the swap wait for it.
 template <typename TIN, typename TOUT, typename TB, bool BIG, bool VEC, int MAXC>
 __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   constexpr int NCU = BIG ? 16 : 8;
@@ -437,14 +470,17 @@ __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   const int64_t last = p.ntiles - 1;
   auto clampt = [&](int64_t x) { return x < p.ntiles ? x : last; };
   ColTile t = col_tile(p, tix);
-  float cr[NCU];
+  uint32_t cw[NCU];
+  float csc[NCU];
   // prologue: first tile and its first stage's coefficients in place
-  coef_fetch<TB, NCU>(p, 0, t, cr);
-  coef_put<NCU>(p, 0, cr, slots);
+  coef_fetch<TB, NCU>(p, 0, t, cw, csc);
+  coef_put<TB, NCU>(p, 0, cw, csc, slots);
   u32x4 pf[MAXC];
+  uint8_t pfs[MAXC];
+  uint32_t smask = 0;
   if constexpr (VEC) {
-    col_prefetch<TIN, MAXC>(p, t, pf);
-    col_swap<TIN, TOUT, MAXC>(p, t, false, true, pf, tile);
+    col_prefetch<TIN, MAXC>(p, t, pf, pfs);
+    col_swap<TIN, TOUT, MAXC>(p, t, false, true, pf, pfs, smask, tile);
   } else {
     col_swap_el<TIN, TOUT>(p, t, false, t, true, tile);
   }
@@ -452,18 +488,21 @@ __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   int sn = 1;
   int64_t tixn = tix;
   if (sn == p.nstage) { sn = 0; tixn = tix + gridDim.x; }
-  coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cr);
-  if constexpr (VEC) col_prefetch<TIN, MAXC>(p, col_tile(p, clampt(tix + gridDim.x)), pf);
+  coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cw, csc);
   __syncthreads();
   int slot = 0;
   while (true) {
     for (int s = 0; s < p.nstage; ++s) {
       // coefficients of the next stage into the other slot, then fetch the
-      // one after
-      if (tixn < p.ntiles) coef_put<NCU>(p, sn, cr, slots + (slot ^ 1) * p.cslot);
+      // one after; the next tile's prefetch goes out behind the first
+      // stage's fetch, so the first two stages never wait for it
+      if (tixn < p.ntiles) coef_put<TB, NCU>(p, sn, cw, csc, slots + (slot ^ 1) * p.cslot);
       ++sn;
       if (sn == p.nstage) { sn = 0; tixn += gridDim.x; }
-      coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cr);
+      coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cw, csc);
+      if constexpr (VEC) {
+        if (s == 0) col_prefetch<TIN, MAXC>(p, col_tile(p, clampt(tix + gridDim.x)), pf, pfs);
+      }
       run_col_tasks<BIG>(p, s, tile, slots + slot * p.cslot, wave, lane);
       __syncthreads();
       slot ^= 1;
@@ -471,12 +510,11 @@ __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
     const int64_t tnx = tix + gridDim.x;
     const bool has_next = tnx < p.ntiles;
     const ColTile nt = col_tile(p, clampt(tnx));
-    if constexpr (VEC) col_swap<TIN, TOUT, MAXC>(p, t, true, has_next, pf, tile);
+    if constexpr (VEC) col_swap<TIN, TOUT, MAXC>(p, t, true, has_next, pf, pfs, smask, tile);
     else col_swap_el<TIN, TOUT>(p, t, true, nt, has_next, tile);
     if (!has_next) break;
     tix = tnx;
     t = nt;
-    if constexpr (VEC) col_prefetch<TIN, MAXC>(p, col_tile(p, clampt(tix + gridDim.x)), pf);
     __syncthreads();
   }
 }

@@ -333,30 +333,55 @@ def _two_sided_small():
     return out
 
 
-@pytest.mark.parametrize("use_ws", [False, True])
-@pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_rotate_weight_small(use_ws, io):
-    c = _two_sided_small()
-    bu, su_ = gpu_blocks(api, c["su"], c["du"], c["tu"], c["gu"], "f32")
-    bv, sv_ = gpu_blocks(api, c["sv"], c["dv"], c["tv"], c["gv"], "f32")
-    ws = torch.empty(api.harp_rotate_weight_workspace(c["du"], c["dv"]) // 4, dtype=torch.float32,
-                     device="cuda") if use_ws else None
+def _rotate_round_trip(c, io, blk, ws, label):
+    bu, su_ = gpu_blocks(api, c["su"], c["du"], c["tu"], c["gu"], blk)
+    bv, sv_ = gpu_blocks(api, c["sv"], c["dv"], c["tv"], c["gv"], blk)
     wd = to_dev(c["w"], io)
-    wt = api.harp_rotate_weight(c["su"], bu, None, signs_dev(c["su_s"]), c["sv"], bv, None, signs_dev(c["sv_s"]),
+    wt = api.harp_rotate_weight(c["su"], bu, su_, signs_dev(c["su_s"]), c["sv"], bv, sv_, signs_dev(c["sv_s"]),
                                 wd, workspace=ws)
     torch.cuda.synchronize()
-    obu = oracle_blocks(c["su"], c["du"], c["tu"], c["gu"], "f32")
-    obv = oracle_blocks(c["sv"], c["dv"], c["tv"], c["gv"], "f32")
+    obu = oracle_blocks(c["su"], c["du"], c["tu"], c["gu"], blk)
+    obv = oracle_blocks(c["sv"], c["dv"], c["tv"], c["gv"], blk)
     ref = O.rotate_weight(c["w"].astype(float), c["su"], obu, c["su_s"].astype(float), c["sv"], obv,
                           c["sv_s"].astype(float))
-    assert_rows_close(from_dev(wt), ref, TOL[io], "two-sided forward")
+    assert_rows_close(from_dev(wt), ref, TOL[io], f"{label} forward")
     wtin = from_dev(wt)
-    back = api.harp_rotate_weight(c["su"], bu, None, signs_dev(c["su_s"]), c["sv"], bv, None,
+    back = api.harp_rotate_weight(c["su"], bu, su_, signs_dev(c["su_s"]), c["sv"], bv, sv_,
                                   signs_dev(c["sv_s"]), wt, inverse=True, workspace=ws)
     torch.cuda.synchronize()
     ref_b = O.rotate_weight(wtin, c["su"], obu, c["su_s"].astype(float), c["sv"], obv, c["sv_s"].astype(float),
                             inverse=True)
-    assert_rows_close(from_dev(back), ref_b, TOL[io], "two-sided inverse")
+    assert_rows_close(from_dev(back), ref_b, TOL[io], f"{label} inverse")
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_small(use_ws, io):
+    # 80 columns: the element path of the column passes (ragged panel)
+    c = _two_sided_small()
+    ws = torch.empty(api.harp_rotate_weight_workspace(c["du"], c["dv"]) // 4, dtype=torch.float32,
+                     device="cuda") if use_ws else None
+    _rotate_round_trip(c, io, "f32", ws, "two-sided")
+
+
+@pytest.mark.parametrize("blk", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_block_types(blk, io):
+    # U (8, 8, 8) on 512 rows and 128 columns: whole panels, the 16-byte path
+    # of the column passes, with every stored block type (the coefficient
+    # words are decoded in the kernel as they go into LDS)
+    print(f"\n[case] two-sided block types blk={blk} io={io}", flush=True)
+    rng = np.random.default_rng(37)
+    su, sv, du, dv = (8, 8, 8), (8, 16), 512, 128
+    c = {"su": su, "sv": sv, "du": du, "dv": dv}
+    c["tu"] = rng.standard_normal(sum(O.theta_counts(su, du))) * 0.05
+    c["tv"] = rng.standard_normal(sum(O.theta_counts(sv, dv))) * 0.05
+    c["gu"] = np.zeros(0)
+    c["gv"] = np.zeros(0)
+    c["su_s"] = np.where(rng.integers(0, 2, du) == 1, 1, -1).astype(np.int8)
+    c["sv_s"] = np.where(rng.integers(0, 2, dv) == 1, 1, -1).astype(np.int8)
+    c["w"] = W.round_io((rng.standard_normal((du, dv)) * 0.02).astype(np.float32), io)
+    _rotate_round_trip(c, io, blk, None, f"two-sided {blk}/{io}")
 
 
 def test_rotate_weight_full_size_sampled():
