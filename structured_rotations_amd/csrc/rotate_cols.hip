@@ -122,8 +122,7 @@ __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColT
       cw[u] = (uint32_t)(int)*src;
       csc[u] = scales[gl * sufi];
     }
-  }
-}
+  }}
 
 // Writes the fetched coefficients into a slot as C[gl][o][k] in fp32 with
 // rows padded to 4 floats (the layout the stage tasks read).
@@ -609,16 +608,34 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   // up to 1024, as wide as fits next to two coefficient slots in 80 KiB (two
   // workgroups per CU) or, failing that, in 160 KiB; among those the widest
   // that divides the column count (whole panels take the 16-byte path).
+  //
+  // Among the dividing widths, the 16-byte path gives every thread the same
+  // number of chunk slots (4 or 8 for bf16 input, 8 or 16 for fp32), and a
+  // slot past the tile's chunks loads and stores its thread's first chunk
+  // again; a width whose chunk count fills its slots best is taken (ties go
+  // to the wider), so the repeated streaming stores stay few.
   auto fits = [&](int w, size_t cap) { return (size_t)nsub * (w + 2 * cw) * sizeof(float) <= cap; };
   const size_t cap = fits(256, (size_t)80 * 1024) ? (size_t)80 * 1024 : (size_t)160 * 1024;
-  int pw = 0, pw_div = 0;
+  const int vi_c = 16 / io_bytes(in_dt);
+  const int lo_c = in_dt == DT::F32 ? 8 : 4;
+  auto slot_waste = [&](int w) {   // slots per chunk of the 16-byte path
+    const int64_t chunks = (int64_t)nsub * (w / vi_c);
+    const int64_t need = (chunks + 511) / 512;
+    if (need > 2 * lo_c) return 1e9;   // element path
+    return (double)(512 * (need <= lo_c ? lo_c : 2 * lo_c)) / (double)chunks;
+  };
+  int pw = 0;
   for (int w = 64; w <= 1024; w += 64) {
     if (!fits(w, cap)) break;
     pw = w;
-    if (ncols % w == 0) pw_div = w;
   }
   if (pw == 0) return hipErrorInvalidValue;
-  if (pw_div >= pw / 2) pw = pw_div;
+  int pw_div = 0;
+  for (int w = 64; w <= pw; w += 64) {
+    if (ncols % w != 0 || w < pw / 2) continue;
+    if (pw_div == 0 || slot_waste(w) <= slot_waste(pw_div)) pw_div = w;
+  }
+  if (pw_div > 0) pw = pw_div;
   p.pw = pw;
   p.mag_ncb = mag(pw / 64);
   p.ncols = ncols;
