@@ -538,11 +538,21 @@ template <typename TIN> struct ColMaxc;
 template <> struct ColMaxc<uint16_t> { static constexpr int lo = 4, hi = 8; };
 template <> struct ColMaxc<float> { static constexpr int lo = 8, hi = 16; };
 
+// fp32 in, bf16 out never takes the 16-byte path (see the launch), so it has
+// no 16-byte kernels.
+template <typename TIN, typename TOUT>
+constexpr bool col_vec_io() { return !(std::is_same<TIN, float>::value && std::is_same<TOUT, uint16_t>::value); }
+
 template <typename TIN, typename TOUT, typename TB, bool BIG>
 hipError_t launch_cols_k(const ColParams& p, int maxc, int grid, size_t lds, hipStream_t st) {
-  void (*kern)(ColParams) = !p.vec                      ? col_pass_kernel<TIN, TOUT, TB, BIG, false, 1>
-                            : maxc <= ColMaxc<TIN>::lo ? col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::lo>
-                                                       : col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::hi>;
+  void (*kern)(ColParams) = col_pass_kernel<TIN, TOUT, TB, BIG, false, 1>;
+  if constexpr (col_vec_io<TIN, TOUT>()) {
+    if (p.vec)
+      kern = maxc <= ColMaxc<TIN>::lo ? col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::lo>
+                                      : col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::hi>;
+  } else {
+    if (p.vec) return hipErrorInvalidValue;
+  }
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
