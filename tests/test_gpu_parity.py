@@ -384,6 +384,25 @@ def test_rotate_weight_block_types(blk, io):
     _rotate_round_trip(c, io, blk, None, f"two-sided {blk}/{io}")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_radix16_column_path(io):
+    # U (16, 8) on 128 rows and 256 columns: a radix above 8 in a column run
+    # (the kernel with radices 9..16 compiled in) on the 16-byte path
+    print(f"\n[case] two-sided radix-16 column run io={io}", flush=True)
+    rng = np.random.default_rng(41)
+    su, sv, du, dv = (16, 8), (16, 16), 128, 256
+    c = {"su": su, "sv": sv, "du": du, "dv": dv}
+    c["tu"] = rng.standard_normal(sum(O.theta_counts(su, du))) * 0.05
+    c["tv"] = rng.standard_normal(sum(O.theta_counts(sv, dv))) * 0.05
+    c["gu"] = np.zeros(0)
+    c["gv"] = np.zeros(0)
+    c["su_s"] = np.where(rng.integers(0, 2, du) == 1, 1, -1).astype(np.int8)
+    c["sv_s"] = np.where(rng.integers(0, 2, dv) == 1, 1, -1).astype(np.int8)
+    c["w"] = W.round_io((rng.standard_normal((du, dv)) * 0.02).astype(np.float32), io)
+    for blk in ("f32", "i8"):
+        _rotate_round_trip(c, io, blk, None, f"two-sided radix 16 {blk}/{io}")
+
+
 def test_rotate_weight_full_size_sampled():
     w = _case("two_sided_13824x5120_bf16")
     su, sv, du, dv = w["su"], w["schedule"], w["d_out"], w["d"]
