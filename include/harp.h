@@ -197,7 +197,7 @@ harp_status harp_apply_inverse(const harp_schedule* s, int64_t d,
  * harp_apply_decode_workspace() gives the bytes needed (rows * d * 4, or 0
  * when the whole row fits one workgroup and a single launch is made), or -1
  * if no split of the schedule fits (then harp_apply_decode returns
- * HARP_ERR_UNSUPPORTED).  workspace: device memory owned by the caller,
+ * HARP_ERR_UNSUPPORTED) or rows * d * 4 does not fit in int64_t.  workspace: device memory owned by the caller,
  * 4-byte aligned, not overlapping x or y; its contents are scratch.  Calls
  * that share one workspace must not overlap in time.  x and y may be the same
  * buffer (with ldx == ldy).  Other arguments, layouts and errors as
@@ -233,7 +233,8 @@ harp_status harp_apply_decode(const harp_schedule* s, int64_t d,
  *   workspace: at least harp_apply_vjp_workspace() bytes of device memory,
  *   4-byte aligned, owned by the caller (x_1 .. x_{m-1} and two gradient rows
  *   in fp32, plus the partial sums).  Every radix must be at most 8 (else
- *   HARP_ERR_UNSUPPORTED, and harp_apply_vjp_workspace() returns -1).
+ *   HARP_ERR_UNSUPPORTED, and harp_apply_vjp_workspace() returns -1; it also
+ *   returns -1 when the size would not fit in int64_t).
  *   rows must be at least 1.
  * harp_theta_vjp: dtheta (harp_theta_count() fp64, theta's layout) from
  *   dblocks through B = Q(theta) G: dL/dQ = dL/dB G^T; Givens

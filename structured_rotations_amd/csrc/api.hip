@@ -195,7 +195,8 @@ harp_status harp_apply_vjp(const harp_schedule* s, int64_t d, const void* blocks
   if ((block_dtype == HARP_I8) != (block_scales != nullptr))
     return fail(HARP_ERR_INVALID_ARG, "block_scales must be given exactly for HARP_I8 blocks");
   const int64_t need = harp::vjp_workspace_bytes(pl, rows < 0 ? 0 : rows);
-  if (need < 0) return fail(HARP_ERR_UNSUPPORTED, "harp_apply_vjp supports radices up to 8");
+  if (need < 0)
+    return fail(HARP_ERR_UNSUPPORTED, "harp_apply_vjp needs every radix <= 8 and a workspace size that fits in int64");
   const int eb = io_dtype == HARP_F32 ? 4 : 2;
   err = harp::check_rows(x, ldx, dy, lddy, rows, d, eb);
   if (!err.empty()) return fail(HARP_ERR_INVALID_ARG, "x/dy: " + err);

@@ -686,6 +686,7 @@ int64_t decode_workspace_bytes(const Plan& pl, DT bdt, int64_t rows) {
   Run runs[2];
   const int n = plan_runs(pl, bdt, runs);
   if (n == 0) return -1;
+  if (rows > (INT64_MAX / 4) / pl.d) return -1;   // size not representable
   return n == 1 ? 0 : rows * pl.d * 4;
 }
 

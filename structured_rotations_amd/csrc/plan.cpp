@@ -1,6 +1,7 @@
 // Host-side schedule planning and argument validation (plain C++, no HIP).
 #include "plan.h"
 
+#include <cstdint>
 #include <cstdio>
 
 namespace harp {
@@ -72,6 +73,7 @@ std::string check_rows(const void* x, int64_t ldx, const void* y, int64_t ldy,
   if (rows < 0) return "rows < 0";
   if (rows == 0) return "";
   if (x == nullptr || y == nullptr) return "x or y is NULL with rows > 0";
+  if (d < 1) return "d < 1";
   if (ldx < d || ldy < d) {
     std::snprintf(buf, sizeof buf, "leading dimension smaller than d (ldx=%lld ldy=%lld d=%lld)",
                   (long long)ldx, (long long)ldy, (long long)d);
@@ -81,12 +83,21 @@ std::string check_rows(const void* x, int64_t ldx, const void* y, int64_t ldy,
   const auto uy = reinterpret_cast<uintptr_t>(y);
   if (ux % elem_bytes != 0 || uy % elem_bytes != 0) return "x or y not aligned to its element size";
   if (x == y && ldx != ldy) return "in-place call (x == y) needs ldx == ldy";
-  if (x != y) {
-    // reject partial overlap: the byte ranges intersect but the bases differ
-    const uint64_t ex = ux + (uint64_t)((rows - 1) * ldx + d) * elem_bytes;
-    const uint64_t ey = uy + (uint64_t)((rows - 1) * ldy + d) * elem_bytes;
-    if (ux < ey && uy < ex) return "x and y overlap without being the same buffer";
-  }
+  // byte extent (rows - 1) * ld + d elements of each buffer, which must fit
+  // in the address space above its base
+  auto extent = [&](uintptr_t base, int64_t ld, uint64_t* end) {
+    if (rows - 1 > (INT64_MAX - d) / ld) return false;
+    const int64_t el = (rows - 1) * ld + d;
+    if (el > INT64_MAX / elem_bytes) return false;
+    const uint64_t bytes = (uint64_t)el * (uint64_t)elem_bytes;
+    if ((uint64_t)base > UINT64_MAX - bytes) return false;
+    *end = (uint64_t)base + bytes;
+    return true;
+  };
+  uint64_t ex = 0, ey = 0;
+  if (!extent(ux, ldx, &ex) || !extent(uy, ldy, &ey)) return "rows x leading dimension exceeds the address space";
+  // reject partial overlap: the byte ranges intersect but the bases differ
+  if (x != y && ux < ey && uy < ex) return "x and y overlap without being the same buffer";
   return "";
 }
 

@@ -289,6 +289,8 @@ hipError_t launch_stage_any(bool fwd, DT bdt, const VjpArgs& a, hipStream_t st) 
 int64_t vjp_workspace_bytes(const Plan& pl, int64_t rows) {
   for (int t = 0; t < pl.m; ++t)
     if (pl.radix[t] > 8) return -1;
+  // at most (m + 1) + 16 fp32 values per row element: keep 4x that in int64
+  if (rows > (INT64_MAX / 256) / pl.d) return -1;
   const int64_t acts = (int64_t)(pl.m - 1) * rows * pl.d;
   const int64_t gbuf = (pl.m > 1 ? 2 : 0) * rows * pl.d;
   const int64_t part = (int64_t)vjp_chunks(pl, rows) * pl.n_blk;

@@ -175,6 +175,14 @@ def test_decode_workspace_sizes_on_host(lib):
     assert ws(ctypes.byref(Schedule.of((8, 8))), 64, _lib.HARP_F32, 5) == 0      # one launch
     assert ws(ctypes.byref(Schedule.of((8, 8))), 65, _lib.HARP_F32, 5) == -1     # not a factorisation
     assert ws(ctypes.byref(Schedule.of((8, 8))), 64, 7, 5) == -1                 # bad dtype
+    # a size that does not fit in int64 is -1, not a wrapped number
+    assert ws(ctypes.byref(Schedule.of((8, 8, 8, 8))), 4096, _lib.HARP_F32, 1 << 62) == -1
+
+
+def test_row_extent_overflow_rejected_on_host(lib):
+    # rows x leading dimension past the address space: an error, before any launch
+    big = (1 << 62) // 4096
+    assert _apply(lib, schedule=(8, 8), d=64, rows=big, ldx=1 << 40, ldy=1 << 40) == _lib.HARP_ERR_INVALID_ARG
 
 
 def test_decode_rejects_on_host(lib):
@@ -202,6 +210,7 @@ def test_vjp_rejects_on_host(lib):
     need = lib.harp_apply_vjp_workspace(s, 4096, 5)
     assert need > 5 * 4096 * 4 * 5       # three activations + two gradient rows + partial sums
     assert lib.harp_apply_vjp_workspace(ctypes.byref(Schedule.of((16, 16))), 256, 5) == -1
+    assert lib.harp_apply_vjp_workspace(s, 4096, 1 << 60) == -1      # size past int64
     vjp = lib.harp_apply_vjp
     args = lambda **kw: [s, 4096, kw.get("blocks", FAKE), kw.get("bdt", 0), kw.get("scales", None), None,
                          FAKE, 4096, FAKE2, 4096, kw.get("dx", None), 4096, kw.get("rows", 5), kw.get("io", 1),
