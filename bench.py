@@ -11,7 +11,9 @@ resident in HBM.  Block materialisation (theta -> blocks, on the GPU) is setup
 and is not timed.  Prints one JSON line.
 
 value = rows/s of the whole job (K steps timed back to back, bracketed by
-device synchronisation).  roofline.achieved = algorithmic bytes per launch
+device synchronisation).  The defaults (W = 50 warm-up steps, K = 200) let
+the GPU reach its steady clocks before the timed steps: after 5 warm-up
+steps the first few dozen launches run up to 10% slower.  roofline.achieved = algorithmic bytes per launch
 (rows * d * 2 bytes read + rows * d * 2 bytes written) / the kernel's mean
 duration, measured with HIP events recorded on the stream the kernel runs on.
 cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
@@ -373,8 +375,8 @@ def materialize_main(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="cayley4096_bf16")
     ap.add_argument("--blk", default="f32", choices=["f32", "bf16", "i8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
