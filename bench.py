@@ -36,6 +36,7 @@ quantisation of the parameters (setup work, not part of a step).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -155,12 +156,17 @@ def latency_main(args) -> int:
                 call()
             stream.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            # no garbage-collector pass inside the timed calls (as timeit does):
+            # one pass over the setup's objects cost up to 40 ms of host time
+            gc.collect()
+            gc.disable()
             t0 = time.perf_counter()
             e0.record(stream)
             for _ in range(steps):
                 call()
             e1.record(stream)
             host_s = time.perf_counter() - t0
+            gc.enable()
             stream.synchronize()
             eager_us = e0.elapsed_time(e1) * 1e3 / steps
             y_eager = y.clone()
@@ -462,6 +468,8 @@ def main() -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()   # re-enabled after the timed steps
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -472,6 +480,7 @@ def main() -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     total_ms = t_start.elapsed_time(t_end)
     per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     flushed = None
