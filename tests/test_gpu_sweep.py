@@ -131,3 +131,61 @@ def test_sweep_rht(idx, inverse):
     torch.cuda.synchronize()
     ref = O.rht_compose(x.astype(np.float64), np.asarray(signs, dtype=float).reshape(k, d), inverse=inverse)
     assert_rows_close(from_dev(y), ref, TOL[io], "rht_compose")
+
+
+def _large_cases(n, seed=99):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        m = int(rng.integers(2, 7))
+        sch = tuple(int(b) for b in rng.choice(RADICES, m))
+        d = int(np.prod(sch))
+        if 4096 < d <= 16384 and (sch, d) not in out:
+            out.append((sch, d))
+    return out
+
+
+LARGE = _large_cases(8)
+
+
+@pytest.mark.parametrize("idx", range(len(LARGE)))
+def test_sweep_large_d(idx):
+    # d from 4097 to 16384 in random mixed-radix orders; row counts on both
+    # sides of the decode entry point's hand-over to the row kernels (128)
+    sch, d = LARGE[idx]
+    rows = [1, 7, 64, 129, 300][idx % 5]
+    io = ["f32", "bf16"][idx % 2]
+    blk = ["f32", "bf16", "i8"][idx % 3]
+    print(f"\n[case] large-d sweep {idx}: schedule {sch} d={d} rows={rows} io={io} blocks={blk}", flush=True)
+    g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 900 + idx)
+    theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
+    gauss = I.gauss_mats(g_gauss, sch)
+    signs = I.rademacher(g_sign, d)
+    x = g_data.standard_normal((rows, d)).astype(np.float32)
+    if io == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    blocks_g, scales_g = gpu_blocks(api, sch, d, theta, gauss, blk)
+    blocks_o = oracle_blocks(sch, d, theta, gauss, blk)
+    sg, s = signs_dev(signs), signs.astype(float)
+    xd = to_dev(x, io)
+    y = api.harp_apply(sch, d, blocks_g, scales_g, sg, xd)
+    yd = api.harp_apply_decode(sch, d, blocks_g, scales_g, sg, xd)
+    torch.cuda.synchronize()
+    y_ref = O.apply(x.astype(np.float64), sch, blocks_o, s)
+    assert_rows_close(from_dev(y), y_ref, TOL[io], "harp_apply")
+    assert_rows_close(from_dev(yd), y_ref, TOL[io], "harp_apply_decode")
+    yin = from_dev(y)
+    xi = api.harp_apply_inverse(sch, d, blocks_g, scales_g, sg, y)
+    torch.cuda.synchronize()
+    assert_rows_close(from_dev(xi), O.apply_inverse(yin, sch, blocks_o, s), TOL[io], "harp_apply_inverse")
+    if max(sch) <= 8:
+        dy = np.random.default_rng(idx).standard_normal((rows, d)).astype(np.float32)
+        if io == "bf16":
+            dy = torch.from_numpy(dy).to(torch.bfloat16).float().numpy()
+        dx, db = api.harp_apply_vjp(sch, d, blocks_g, scales_g, sg, xd, to_dev(dy, io))
+        torch.cuda.synchronize()
+        rdx, rdb = O.apply_vjp(x.astype(np.float64), sch, blocks_o, s, dy.astype(np.float64))
+        assert_rows_close(from_dev(dx), rdx, TOL[io], "vjp dx")
+        ref = np.concatenate([b.ravel() for b in rdb])
+        got = db.cpu().numpy().astype(np.float64)
+        assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref), "vjp dB"
