@@ -393,8 +393,8 @@ def main() -> int:
     ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize", "vjp"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the apply path has no cross-GPU step and this build runs on a "
-              "single MI355X; run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the apply path has no cross-GPU step (rows are independent; "
+              "sharding is by rows); run with --gpus 1.", file=sys.stderr)
         return 2
     if args.mode == "latency":
         return latency_main(args)
