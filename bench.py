@@ -544,10 +544,33 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "parity_max_row_rel_l2": parity,
     }
+    if not args.copy_calibration:
+        line["copy_ceiling"] = copy_ceiling(x, y, stream, achieved)
     if not args.no_cpu_baseline and not args.copy_calibration:
         line["cpu_baseline"] = cpu_baseline(w, args.blk)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def copy_ceiling(x, y, stream, achieved_gbps: float, launches: int = 50) -> dict:
+    """A plain device copy of the step's input into its output buffer (the
+    same bytes read and written), timed like the kernel after the timed
+    region: the practical HBM ceiling for this traffic pattern."""
+    import torch
+
+    nbytes = 2 * x.numel() * x.element_size()
+    for _ in range(10):
+        y.copy_(x)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in ev:
+        a.record(stream)
+        y.copy_(x)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"what": "torch device copy, same bytes in and out", "achieved_GBps": round(gbps, 1),
+            "kernel_frac_of_copy": round(achieved_gbps / gbps, 4)}
 
 
 if __name__ == "__main__":
