@@ -107,14 +107,39 @@ def cpu_baseline(w: dict, blk: str, budget_s: float = 30.0) -> dict:
         x = w["x"]
         n = x.shape[0]
         chunk = 2048
-        t0 = time.perf_counter()
-        done = 0
-        while done < n and time.perf_counter() - t0 < budget_s:
-            O.apply(x[done:done + chunk].astype(np.float64), w["schedule"], blocks, w["signs"].astype(float))
-            done += min(chunk, n - done)
-        dt = time.perf_counter() - t0
-        return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread"}
+
+        def run(limit_s):
+            t0 = time.perf_counter()
+            done = 0
+            while done < n and time.perf_counter() - t0 < limit_s:
+                O.apply(x[done:done + chunk].astype(np.float64), w["schedule"], blocks, w["signs"].astype(float))
+                done += min(chunk, n - done)
+            return done, time.perf_counter() - t0
+
+        done, dt = run(budget_s)
+    out = {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread", "host": host_info()}
+    # the same oracle with numpy's default thread pool (context only)
+    n = done
+    done, dt = run(budget_s)
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    out["all_cores"] = {"value": round(done / dt, 1), "unit": "rows/s", "cores": threads,
+                        "sample": f"first {done} rows, fp64 numpy, default thread pool"}
+    return out
+
+
+def host_info() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 LAT_ROWS = (1, 2, 4, 8, 16, 32, 64, 128)
@@ -533,6 +558,7 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
         "kernel_ms_mean": round(kern_ms, 5),
+        "kernel_ms_median": round(float(np.median(per_launch)), 5),
         "kernel_ms_p10_p90": [round(float(np.percentile(per_launch, 10)), 5),
                               round(float(np.percentile(per_launch, 90)), 5)],
         "alg_bytes_per_launch": alg_bytes,
