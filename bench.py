@@ -527,7 +527,7 @@ def main() -> int:
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
 
     # spot parity check of the benchmarked output against the oracle (8 rows)
-    parity = None
+    parity = roundtrip = None
     if not args.copy_calibration and wl.kind == "apply":
         from oracle import harp_oracle as O
         idx = np.array([0, rows // 3, rows // 2, rows - 1])
@@ -535,6 +535,10 @@ def main() -> int:
         ref = O.apply(w["x"][idx].astype(np.float64), sch, ob, w["signs"].astype(float))
         got = y[torch.from_numpy(idx).cuda()].float().cpu().numpy()
         parity = float(O.row_rel_l2(got, ref).max())
+        # round trip of the whole batch through the inverse (one more launch, untimed)
+        xb = api.harp_apply_inverse(sch, d, blocks, scales, sg, y)
+        torch.cuda.synchronize()
+        roundtrip = float(O.row_rel_l2(xb.float().cpu().numpy(), x.float().cpu().numpy()).max())
 
     unit = {"apply": "rows/s", "rht": "rows/s", "two_sided": "weights/s"}[wl.kind]
     traffic = None if args.copy_calibration else traffic_from_profile(args.workload, args.blk)
@@ -569,6 +573,7 @@ def main() -> int:
         "kernel_ms_mean_flushed": None if flushed is None else round(float(flushed.mean()), 5),
         "wall_s_timed": round(wall, 4),
         "parity_max_row_rel_l2": parity,
+        "roundtrip_max_row_rel_l2": roundtrip,
     }
     if not args.copy_calibration:
         line["copy_ceiling"] = copy_ceiling(x, y, stream, achieved)
