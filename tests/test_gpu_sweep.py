@@ -88,7 +88,8 @@ def test_sweep_two_sided(idx, use_ws):
     su, sv = TWO_SIDED[idx]
     du, dv = int(np.prod(su)), int(np.prod(sv))
     io = ["f32", "bf16"][idx % 2]
-    print(f"\n[case] two-sided sweep {idx}: U {su} V {sv} io={io} workspace={use_ws}", flush=True)
+    print(f"\n[case] two-sided sweep {idx}: U {su} V {sv} io={io} workspace={use_ws} "
+          f"blocks={['f32', 'bf16', 'i8'][(idx + int(use_ws)) % 3]}", flush=True)
     g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 600 + idx)
     tu, tv = I.theta_params(g_theta, su, du, 0.05, 0.1), I.theta_params(g_theta, sv, dv, 0.05, 0.1)
     gu, gv = I.gauss_mats(g_gauss, su), I.gauss_mats(g_gauss, sv)
@@ -96,15 +97,16 @@ def test_sweep_two_sided(idx, use_ws):
     w = g_data.standard_normal((du, dv)).astype(np.float32)
     if io == "bf16":
         w = torch.from_numpy(w).to(torch.bfloat16).float().numpy()
-    bu, _ = gpu_blocks(api, su, du, tu, gu, "f32")
-    bv, _ = gpu_blocks(api, sv, dv, tv, gv, "f32")
+    blk = ["f32", "bf16", "i8"][(idx + int(use_ws)) % 3]
+    bu, scu = gpu_blocks(api, su, du, tu, gu, blk)
+    bv, scv = gpu_blocks(api, sv, dv, tv, gv, blk)
     ws = None
     if use_ws:
         ws = torch.empty(api.harp_rotate_weight_workspace(du, dv), dtype=torch.uint8, device="cuda")
-    wt = api.harp_rotate_weight(su, bu, None, signs_dev(s_u), sv, bv, None, signs_dev(s_v), to_dev(w, io),
+    wt = api.harp_rotate_weight(su, bu, scu, signs_dev(s_u), sv, bv, scv, signs_dev(s_v), to_dev(w, io),
                                 workspace=ws)
     torch.cuda.synchronize()
-    obu, obv = oracle_blocks(su, du, tu, gu, "f32"), oracle_blocks(sv, dv, tv, gv, "f32")
+    obu, obv = oracle_blocks(su, du, tu, gu, blk), oracle_blocks(sv, dv, tv, gv, blk)
     ref = O.rotate_weight(w.astype(np.float64), su, obu, s_u.astype(float), sv, obv, s_v.astype(float))
     # bf16 without a workspace rounds between the passes (three roundings)
     tol = TOL[io] if (io == "f32" or use_ws) else TOL["bf16"]
