@@ -13,9 +13,10 @@ and is not timed.  Prints one JSON line.
 value = rows/s of the whole job (K steps timed back to back, bracketed by
 device synchronisation).  The defaults (W = 50 warm-up steps, K = 200) let
 the GPU reach its steady clocks before the timed steps: after 5 warm-up
-steps the first few dozen launches run up to 10% slower.  roofline.achieved = algorithmic bytes per launch
-(rows * d * 2 bytes read + rows * d * 2 bytes written) / the kernel's mean
-duration, measured with HIP events recorded on the stream the kernel runs on.
+steps the first few dozen launches run up to 10% slower.
+roofline.achieved = algorithmic bytes per launch (rows * d * 2 bytes read +
+rows * d * 2 bytes written) / the kernel's mean duration, measured with HIP
+events recorded on the stream the kernel runs on.
 cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
 
 --mode latency: the per-token (decode) regime, 1 to 64 rows per call, for
@@ -23,7 +24,9 @@ harp_apply_decode and, beside it, harp_apply.  For each row count:
 microseconds per call of K back-to-back calls issued from Python (host launch
 cost included), and of the same calls captured once in a HIP graph and
 replayed (device time per call, launch gaps included); the replay's output is
-checked against the eager calls and both entry points against the oracle.
+checked against the eager calls and the two entry points against each other
+(parity with the oracle is the tests' job; only the cpu_baseline leg runs the
+oracle here).
 
 --mode vjp: the reverse mode used to fit the parameters (dx and the block
 gradients for one batch, then the parameter gradient), milliseconds per call,
@@ -71,6 +74,14 @@ def traffic_from_profile(workload: str, blk: str):
     if rec.get("kernel_hash") != kernel_hash(rec.get("kernel", "")):
         return None
     return rec.get("bytes_per_launch")
+
+
+def row_rel_l2(a, b) -> np.ndarray:
+    """Per-row relative l2 distance ||a - b|| / ||b|| of two row batches."""
+    a = np.atleast_2d(np.asarray(a, dtype=np.float64))
+    b = np.atleast_2d(np.asarray(b, dtype=np.float64))
+    den = np.linalg.norm(b, axis=1)
+    return np.linalg.norm(a - b, axis=1) / np.where(den > 0, den, 1.0)
 
 
 def cpu_baseline(w: dict, blk: str, budget_s: float = 30.0) -> dict:
@@ -150,7 +161,6 @@ def latency_main(args) -> int:
     (the small-batch entry point) and, beside it, harp_apply."""
     import torch
 
-    from oracle import harp_oracle as O
     from structured_rotations_amd import api
     from structured_rotations_amd import workloads as W
 
@@ -169,7 +179,6 @@ def latency_main(args) -> int:
     xall = torch.from_numpy(w["x"]).to(tdt).cuda()
     ws_bytes = api.harp_apply_decode_workspace(sch, d, args.blk, max(LAT_ROWS))
     ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
-    ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
     steps = max(args.steps, 20)
     warm = max(args.warmup, 5)
     stream = torch.cuda.Stream()
@@ -224,9 +233,9 @@ def latency_main(args) -> int:
         dec = measure(lambda: api.harp_apply_decode(sch, d, blocks, scales, sg, x, yd, workspace=ws,
                                                     stream=stream), yd)
         app = measure(lambda: api.harp_apply(sch, d, blocks, scales, sg, x, ya, stream=stream), ya)
-        ref = O.apply(w["x"][:r].astype(np.float64), sch, ob, w["signs"].astype(float))
-        worst = max(worst, float(O.row_rel_l2(yd.float().cpu().numpy(), ref).max()),
-                    float(O.row_rel_l2(ya.float().cpu().numpy(), ref).max()))
+        # the two entry points compute the same transform (parity with the
+        # oracle is the tests' job): their outputs agree to rounding
+        worst = max(worst, float(row_rel_l2(yd.float().cpu().numpy(), ya.float().cpu().numpy()).max()))
         table.append({"rows": r,
                       "decode_us_graph": round(dec[2], 3), "decode_us_eager": round(dec[0], 3),
                       "decode_us_host": round(dec[1], 3),
@@ -245,7 +254,7 @@ def latency_main(args) -> int:
                    "kind": "apply-latency", "parallelism": "single GPU"},
         "coefficient_bytes_per_call": cbytes,
         "rows_table": table,
-        "parity_max_row_rel_l2": worst,
+        "decode_vs_apply_max_row_rel_l2": worst,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -255,7 +264,6 @@ def vjp_main(args) -> int:
     """Reverse mode over one batch: harp_apply_vjp (dx + dB) and harp_theta_vjp."""
     import torch
 
-    from oracle import harp_oracle as O
     from structured_rotations_amd import api
     from structured_rotations_amd import workloads as W
 
@@ -306,12 +314,12 @@ def vjp_main(args) -> int:
         bwd = rd * 3 * eb
     red = nchunk * nblk * 4 * 2 + nblk * 4
     moved = fwd + bwd + red
-    # parity on 4 sampled rows is not defined for a sum over rows; check dx rows instead
-    idx = np.array([0, rows // 2, rows - 1])
-    ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
-    rdx = O.apply_inverse(dy[torch.from_numpy(idx).cuda()].float().cpu().numpy().astype(np.float64), sch, ob,
-                          w["signs"].astype(float))
-    par = float(O.row_rel_l2(dx[torch.from_numpy(idx).cuda()].float().cpu().numpy(), rdx).max())
+    # dx = M^T dy is the inverse transform of dy for orthogonal blocks: the
+    # reverse mode's dx agrees with harp_apply_inverse to rounding (parity
+    # with the oracle is the tests' job)
+    dx_inv = api.harp_apply_inverse(sch, d, blocks, scales, sg, dy)
+    torch.cuda.synchronize()
+    par = float(row_rel_l2(dx.float().cpu().numpy(), dx_inv.float().cpu().numpy()).max())
     line = {
         "metric": "HARP reverse mode (dx + block gradients) over one batch, ms per call",
         "value": round(ms_vjp, 4),
@@ -328,7 +336,7 @@ def vjp_main(args) -> int:
         "io_bytes_x_dy_dx": 3 * rd * eb,
         "ms_theta_vjp": round(ms_theta, 4),
         "chunks": int(nchunk),
-        "parity_dx_max_row_rel_l2": par,
+        "dx_vs_inverse_max_row_rel_l2": par,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -338,7 +346,6 @@ def materialize_main(args) -> int:
     """Block materialisation and int8 parameter quantisation, microseconds per call."""
     import torch
 
-    from oracle import harp_oracle as O
     from structured_rotations_amd import api
     from structured_rotations_amd import workloads as W
 
@@ -377,16 +384,15 @@ def materialize_main(args) -> int:
         t_f = timed(lambda: api.harp_materialize_blocks(sch, d, th, gs, "f32", blk_out))
         t_8 = timed(lambda: api.harp_materialize_blocks_q8(sch, d, codes, tsc, gs, "f32", blk_out))
         torch.cuda.synchronize()
-        c_ref, s_ref = O.quantize_theta(sch, d, theta)
-        ok = bool(np.array_equal(codes.cpu().numpy(), c_ref) and np.array_equal(tsc.cpu().numpy(), s_ref))
-        ex = np.concatenate([b.ravel() for b in O.materialize_blocks(sch, d, O.dequantize_theta(sch, d, c_ref, s_ref),
-                                                                      gauss)])
-        got = blk_out.cpu().numpy().astype(np.float64)
-        err = float(np.max(np.abs(got - ex) / (np.abs(ex) + 1e-30) * (np.abs(ex) > 1e-12)))
+        # how far int8 parameters move the blocks (context; parity is the tests' job)
+        b_f, _ = api.harp_materialize_blocks(sch, d, th, gs, "f32")
+        torch.cuda.synchronize()
+        got, ref = blk_out.cpu().numpy().astype(np.float64), b_f.cpu().numpy().astype(np.float64)
+        shift = float(np.max(np.abs(got - ref)))
         out.append({"side": side or "rows", "schedule": list(sch), "d": d,
                     "n_theta": int(th.numel()), "n_scales": int(tsc.numel()),
                     "us_quantize_theta": t_q, "us_materialize_f64_theta": t_f, "us_materialize_i8_theta": t_8,
-                    "codes_bit_exact": ok, "max_rel_err_blocks_f32": err})
+                    "max_abs_block_change_from_int8_theta": shift})
     line = {
         "metric": "HARP block materialisation from int8 parameters, microseconds per call",
         "value": round(sum(o["us_materialize_i8_theta"] for o in out), 3),
@@ -526,19 +532,13 @@ def main() -> int:
     value = units / (ms_per_step * 1e-3)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
 
-    # spot parity check of the benchmarked output against the oracle (8 rows)
-    parity = roundtrip = None
+    # round trip of the whole batch through the inverse (one more launch,
+    # untimed); parity with the oracle is the tests' and smoke()'s job
+    roundtrip = None
     if not args.copy_calibration and wl.kind == "apply":
-        from oracle import harp_oracle as O
-        idx = np.array([0, rows // 3, rows // 2, rows - 1])
-        ob = O.stored_blocks(O.materialize_blocks(sch, d, w["theta"], w["gauss"]), args.blk)
-        ref = O.apply(w["x"][idx].astype(np.float64), sch, ob, w["signs"].astype(float))
-        got = y[torch.from_numpy(idx).cuda()].float().cpu().numpy()
-        parity = float(O.row_rel_l2(got, ref).max())
-        # round trip of the whole batch through the inverse (one more launch, untimed)
         xb = api.harp_apply_inverse(sch, d, blocks, scales, sg, y)
         torch.cuda.synchronize()
-        roundtrip = float(O.row_rel_l2(xb.float().cpu().numpy(), x.float().cpu().numpy()).max())
+        roundtrip = float(row_rel_l2(xb.float().cpu().numpy(), x.float().cpu().numpy()).max())
 
     unit = {"apply": "rows/s", "rht": "rows/s", "two_sided": "weights/s"}[wl.kind]
     traffic = None if args.copy_calibration else traffic_from_profile(args.workload, args.blk)
@@ -572,7 +572,6 @@ def main() -> int:
                     "frac": round(alg_flops / (kern_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4)},
         "kernel_ms_mean_flushed": None if flushed is None else round(float(flushed.mean()), 5),
         "wall_s_timed": round(wall, 4),
-        "parity_max_row_rel_l2": parity,
         "roundtrip_max_row_rel_l2": roundtrip,
     }
     if not args.copy_calibration:
