@@ -8,7 +8,9 @@ A step is one pass of the hot path over one batch: for the default workload
 (cayley4096_bf16: 16384 rows x 4096, bf16 rows, schedule (8,8,8,8), Cayley
 blocks over Sylvester H8) one harp_apply launch over the whole batch, inputs
 resident in HBM.  Block materialisation (theta -> blocks, on the GPU) is setup
-and is not timed.  Prints one JSON line.
+and is not timed.  Prints one JSON line.  The default workload brings the
+d = 5120 one (mixed5120_bf16: 32768 rows x 5120, (8,8,8,5,2)) along as the
+"d5120" sub-record, measured the same way (--single drops it).
 
 value = rows/s of the whole job (K steps timed back to back, bracketed by
 device synchronisation).  The defaults (W = 50 warm-up steps, K = 200) let
@@ -17,7 +19,11 @@ steps the first few dozen launches run up to 10% slower.
 roofline.achieved = algorithmic bytes per launch (rows * d * 2 bytes read +
 rows * d * 2 bytes written) / the kernel's mean duration, measured with HIP
 events recorded on the stream the kernel runs on.
-cpu_baseline = the fp64 numpy oracle, single-threaded, on the full batch.
+kernel_ms_mean_flushed = the same launches (up to 100), each after a 1 GiB
+write that evicts L2 and the MALL (--no-flush skips it).
+cpu_baseline = the fp64 numpy oracle, single-threaded, on a bounded sample
+(the whole batch when it finishes within 30 s), and its comparison with the
+GPU's output on that sample (oracle_max_row_rel_l2).
 
 --mode latency: the per-token (decode) regime, 1 to 64 rows per call, for
 harp_apply_decode and, beside it, harp_apply.  For each row count:
@@ -52,6 +58,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "cayley4096_bf16"      # 16384 x 4096 bf16 rows, (8,8,8,8)
+SECOND_WORKLOAD = "mixed5120_bf16"        # 32768 x 5120 bf16 rows, (8,8,8,5,2)
 FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 (vector and matrix)
 
 
@@ -84,56 +92,68 @@ def row_rel_l2(a, b) -> np.ndarray:
     return np.linalg.norm(a - b, axis=1) / np.where(den > 0, den, 1.0)
 
 
-def cpu_baseline(w: dict, blk: str, budget_s: float = 30.0) -> dict:
-    """Time the oracle (as it stands) single-threaded on a bounded sample."""
-    from threadpoolctl import threadpool_limits
+def cpu_baseline(w: dict, blk: str, y_gpu, budget_s: float = 30.0) -> dict:
+    """Time the oracle (as it stands) single-threaded on a bounded sample of
+    the workload, and compare its output on that sample with the GPU's output
+    of the timed step (max per-row relative l2; the bound is 4e-3 for bf16
+    rows): the only place this script runs the oracle."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import harp_oracle as O
     kind = w["workload"].kind
+
+    def gpu_rows(lo, hi):
+        return y_gpu[lo:hi].float().cpu().numpy().astype(np.float64)
+
     with threadpool_limits(1):
-        if kind == "rht":
-            x = w["x"].astype(np.float64)
-            n = x.shape[0]
-            chunk = 1024
-            t0 = time.perf_counter()
-            done = 0
-            while done < n and time.perf_counter() - t0 < budget_s:
-                O.rht_compose(x[done:done + chunk], w["signs"].astype(float))
-                done += min(chunk, n - done)
-            dt = time.perf_counter() - t0
-            return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                    "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread"}
         if kind == "two_sided":
             t0 = time.perf_counter()
             bu = O.stored_blocks(O.materialize_blocks(w["su"], w["d_out"], w["theta_u"], w["gauss_u"]), blk)
             bv = O.stored_blocks(O.materialize_blocks(w["schedule"], w["d"], w["theta_v"], w["gauss_v"]), blk)
             t1 = time.perf_counter()
-            O.rotate_weight(w["x"].astype(np.float64), w["su"], bu, w["signs_u"].astype(float), w["schedule"], bv,
-                            w["signs_v"].astype(float))
+            ref = O.rotate_weight(w["x"].astype(np.float64), w["su"], bu, w["signs_u"].astype(float), w["schedule"],
+                                  bv, w["signs_v"].astype(float))
             dt = time.perf_counter() - t1
+            err = float(O.row_rel_l2(gpu_rows(0, ref.shape[0]), ref).max())
             return {"value": 1.0 / dt, "unit": "weights/s", "cores": 1, "kind": "oracle",
                     "sample": f"the full {w['d_out']}x{w['d']} weight, fp64 numpy, 1 thread "
-                              f"(block setup {t1 - t0:.1f}s not counted)"}
-        blocks = O.stored_blocks(O.materialize_blocks(w["schedule"], w["d"], w["theta"], w["gauss"]), blk)
+                              f"(block setup {t1 - t0:.1f}s not counted)",
+                    "oracle_max_row_rel_l2": err, "host": host_info()}
         x = w["x"]
         n = x.shape[0]
-        chunk = 2048
+        if kind == "rht":
+            chunk = 1024
+            signs = w["signs"].astype(float)
 
-        def run(limit_s):
+            def one(lo, hi):
+                return O.rht_compose(x[lo:hi].astype(np.float64), signs)
+        else:
+            chunk = 2048
+            blocks = O.stored_blocks(O.materialize_blocks(w["schedule"], w["d"], w["theta"], w["gauss"]), blk)
+
+            def one(lo, hi):
+                return O.apply(x[lo:hi].astype(np.float64), w["schedule"], blocks, w["signs"].astype(float))
+
+        def run(limit_s, check):
             t0 = time.perf_counter()
-            done = 0
-            while done < n and time.perf_counter() - t0 < limit_s:
-                O.apply(x[done:done + chunk].astype(np.float64), w["schedule"], blocks, w["signs"].astype(float))
-                done += min(chunk, n - done)
-            return done, time.perf_counter() - t0
+            done, worst, t_check = 0, 0.0, 0.0
+            while done < n and time.perf_counter() - t0 - t_check < limit_s:
+                hi = min(n, done + chunk)
+                ref = one(done, hi)
+                if check:
+                    tc = time.perf_counter()
+                    worst = max(worst, float(O.row_rel_l2(gpu_rows(done, hi), ref).max()))
+                    t_check += time.perf_counter() - tc
+                done = hi
+            return done, time.perf_counter() - t0 - t_check, worst
 
-        done, dt = run(budget_s)
+        done, dt, worst = run(budget_s, True)
     out = {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-           "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread", "host": host_info()}
+           "sample": f"first {done} of {n} rows, fp64 numpy, 1 thread",
+           "oracle_max_row_rel_l2": worst, "host": host_info()}
     # the same oracle with numpy's default thread pool (context only)
     n = done
-    done, dt = run(budget_s)
-    from threadpoolctl import threadpool_info
+    done, dt, _ = run(budget_s, False)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     out["all_cores"] = {"value": round(done / dt, 1), "unit": "rows/s", "cores": threads,
                         "sample": f"first {done} rows, fp64 numpy, default thread pool"}
@@ -414,13 +434,16 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="cayley4096_bf16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--blk", default="f32", choices=["f32", "bf16", "i8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of the batch instead (counter calibration)")
-    ap.add_argument("--flush", action="store_true",
-                    help="per-launch timing with L2 and MALL flushed (a 1 GiB write) before every launch")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the second timing pass with L2 and the MALL flushed (a 1 GiB write) before "
+                         "every launch")
+    ap.add_argument("--single", action="store_true",
+                    help="the named workload only (the default workload otherwise brings the d = 5120 one along)")
     ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize", "vjp"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -435,12 +458,30 @@ def main() -> int:
         return vjp_main(args)
 
     import torch
+    torch.cuda.set_device(0)
+    line = throughput(args.workload, args, with_cpu=not args.no_cpu_baseline)
+    if args.workload == DEFAULT_WORKLOAD and not args.copy_calibration and not args.single:
+        # the headline metric names both row lengths: d = 5120 rides along as
+        # a sub-record with the same timing, roofline and counter fields
+        sub = throughput(SECOND_WORKLOAD, args, with_cpu=False)
+        line["d5120"] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
+                                             "kernel_ms_mean", "kernel_ms_median", "kernel_ms_p10_p90",
+                                             "kernel_ms_mean_flushed", "alg_bytes_per_launch", "compute",
+                                             "roundtrip_max_row_rel_l2", "copy_ceiling")}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def throughput(name: str, args, with_cpu: bool) -> dict:
+    """One workload: K timed steps back to back (per-launch HIP events on the
+    launch stream), then the same launches each after an L2/MALL flush, then
+    the untimed checks; returns the JSON record."""
+    import torch
 
     from structured_rotations_amd import api
     from structured_rotations_amd import workloads as W
 
-    torch.cuda.set_device(0)
-    w = W.make(args.workload)
+    w = W.make(name)
     wl = w["workload"]
     d, sch, io = w["d"], w["schedule"], w["io"]
     tdt = torch.bfloat16 if io == "bf16" else torch.float32
@@ -473,8 +514,10 @@ def main() -> int:
         su_s = torch.from_numpy(w["signs_u"]).cuda()
         sv_s = torch.from_numpy(w["signs_v"]).cuda()
 
+        # the rotation as planned for this workload: bf16 between the passes,
+        # in place in the output (no workspace)
         def step():
-            api.harp_rotate_weight(w["su"], bu, scu, su_s, sch, bv, scv, sv_s, x, y)
+            api.harp_rotate_weight(w["su"], bu, scu, su_s, sch, bv, scv, sv_s, x, y, fp32_intermediates=False)
         alg_bytes = rows * d * eb * 2
         # b_t FMAs per element per stage, both sides
         alg_flops = 2 * rows * d * (sum(sch) + sum(w["su"]))
@@ -515,10 +558,11 @@ def main() -> int:
     total_ms = t_start.elapsed_time(t_end)
     per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     flushed = None
-    if args.flush:
+    if not args.no_flush:
         # same launches, each after a 1 GiB write that evicts L2 and the MALL
         scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(args.steps, 100))]
         for a, b in evf:
             scratch.fill_(1.0)
             a.record(stream)
@@ -533,7 +577,7 @@ def main() -> int:
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
 
     # round trip of the whole batch through the inverse (one more launch,
-    # untimed); parity with the oracle is the tests' and smoke()'s job
+    # untimed); the oracle's own check of the output is in cpu_baseline
     roundtrip = None
     if not args.copy_calibration and wl.kind == "apply":
         xb = api.harp_apply_inverse(sch, d, blocks, scales, sg, y)
@@ -541,7 +585,7 @@ def main() -> int:
         roundtrip = float(row_rel_l2(xb.float().cpu().numpy(), x.float().cpu().numpy()).max())
 
     unit = {"apply": "rows/s", "rht": "rows/s", "two_sided": "weights/s"}[wl.kind]
-    traffic = None if args.copy_calibration else traffic_from_profile(args.workload, args.blk)
+    traffic = None if args.copy_calibration else traffic_from_profile(name, args.blk)
     line = {
         "metric": "HARP apply rows/s + achieved HBM GB/s (% of peak), d=4096/5120 bf16",
         "value": round(value, 1),
@@ -555,7 +599,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded Student-t nu=3 rows with outlier channels; random Cayley/Givens parameters)",
-        "config": {"workload": args.workload if not args.copy_calibration else "device copy of " + args.workload,
+        "config": {"workload": name if not args.copy_calibration else "device copy of " + name,
                    "rows": rows, "d": d, "schedule": list(sch), "io": io, "blocks": args.blk,
                    "kind": wl.kind, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -576,10 +620,11 @@ def main() -> int:
     }
     if not args.copy_calibration:
         line["copy_ceiling"] = copy_ceiling(x, y, stream, achieved)
-    if not args.no_cpu_baseline and not args.copy_calibration:
-        line["cpu_baseline"] = cpu_baseline(w, args.blk)
-    print(json.dumps(line), flush=True)
-    return 0
+    if wl.kind == "two_sided":
+        line["config"]["intermediates"] = "bf16, in place"
+    if with_cpu and not args.copy_calibration:
+        line["cpu_baseline"] = cpu_baseline(w, args.blk, y)
+    return line
 
 
 def copy_ceiling(x, y, stream, achieved_gbps: float, launches: int = 50) -> dict:

@@ -194,11 +194,13 @@ harp_status harp_apply_inverse(const harp_schedule* s, int64_t d,
  * through `workspace`, so the arithmetic is fp32 throughout as in harp_apply.
  * Above 128 rows the call runs harp_apply's row kernels instead (faster at
  * those sizes); the workspace is then left untouched.
- * harp_apply_decode_workspace() gives the bytes needed (rows * d * 4, or 0
- * when the whole row fits one workgroup and a single launch is made), or -1
- * if no split of the schedule fits (then harp_apply_decode returns
- * HARP_ERR_UNSUPPORTED) or rows * d * 4 does not fit in int64_t.  workspace: device memory owned by the caller,
- * 4-byte aligned, not overlapping x or y; its contents are scratch.  Calls
+ * harp_apply_decode_workspace() gives the bytes needed: rows * d * 4; 0
+ * when the whole row fits one workgroup and a single launch is made, or when
+ * rows > 128 (the row kernels need no hand-off); -1 if no split of the
+ * schedule fits (then harp_apply_decode returns HARP_ERR_UNSUPPORTED) or
+ * rows * d * 4 does not fit in int64_t.  workspace: device memory owned by
+ * the caller, 4-byte aligned, not overlapping x or y; its contents are
+ * scratch; NULL is accepted whenever the size is 0.  Calls
  * that share one workspace must not overlap in time.  x and y may be the same
  * buffer (with ldx == ldy).  Other arguments, layouts and errors as
  * harp_apply; rows == 0 returns HARP_OK without a launch.
@@ -267,9 +269,9 @@ harp_status harp_theta_vjp(const harp_schedule* s, int64_t d,
  * W_out has row stride ldo.  io_dtype F32 or BF16 for both.  blocks_u /
  * blocks_v use the common block_dtype (scales non-NULL exactly for I8).
  * workspace: NULL, or at least harp_rotate_weight_workspace(d_out, d_in)
- *   bytes.  With a workspace the intermediate passes are kept in fp32; with
- *   NULL they run in place in w_out and are rounded to io_dtype between
- *   passes.  w and w_out may be the same buffer (with ldw == ldo).
+ *   bytes, 16-byte aligned (else HARP_ERR_INVALID_ARG).  With a workspace the
+ *   intermediate passes are kept in fp32; with NULL they run in place in
+ *   w_out and are rounded to io_dtype between passes.  w and w_out may be the same buffer (with ldw == ldo).
  * ---------------------------------------------------------------------- */
 size_t harp_rotate_weight_workspace(int64_t d_out, int64_t d_in);
 harp_status harp_rotate_weight(const harp_schedule* su, const void* blocks_u,

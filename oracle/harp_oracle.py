@@ -45,11 +45,11 @@ import numpy as np
 
 __all__ = [
     "is_pow2", "sylvester", "qr_fallback", "mgs_qr", "givens", "cayley",
-    "theta_counts", "gauss_stage_list", "materialize_blocks", "stage_strides",
+    "theta_counts", "gauss_stage_list", "materialize_blocks",
     "theta_groups", "quantize_theta", "dequantize_theta",
     "apply", "apply_inverse", "apply_vjp", "theta_vjp", "dense_operator", "fwht", "rht_compose",
     "rotate_weight", "round_bf16", "round_f32", "quantize_i8", "stored_blocks",
-    "row_rel_l2", "unpack_bf16",
+    "row_rel_l2",
 ]
 
 
@@ -247,14 +247,6 @@ def dequantize_theta(schedule, d: int, codes: np.ndarray, scales: np.ndarray) ->
 # --------------------------------------------------------------------------
 # the structured transform
 # --------------------------------------------------------------------------
-
-def stage_strides(schedule) -> list[int]:
-    """Stride of digit t in a C-order mixed-radix index (reading R1)."""
-    out = []
-    for t in range(len(schedule)):
-        out.append(int(np.prod(schedule[t + 1:])) if t + 1 < len(schedule) else 1)
-    return out
-
 
 def _stage(x: np.ndarray, schedule, t: int, bt: np.ndarray, transpose: bool) -> np.ndarray:
     """One stage: the block of group c acts along digit t [TS §2.1, §2.2].
@@ -476,12 +468,6 @@ def round_bf16(v):
     if np.any(tiny):
         raise ValueError("round_bf16: subnormal bfloat16 range not modelled")
     return out
-
-
-def unpack_bf16(bits: np.ndarray) -> np.ndarray:
-    """Widen raw bfloat16 bit patterns (uint16) to fp64."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
 
 
 def quantize_i8(bt: np.ndarray):

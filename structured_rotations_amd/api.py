@@ -34,6 +34,37 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _flat(t, name, dtype, count):
+    """A parameter array: the given dtype, contiguous, exactly count elements
+    (the C side receives only a pointer and cannot check any of this)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if count < 0:
+        raise ValueError(f"{name}: the schedule does not factor d")
+    if t.numel() != count:
+        raise ValueError(f"{name} has {t.numel()} elements, the schedule needs {count}")
+
+
+def _block_params(schedule, d, blocks, scales, signs, name=""):
+    """blocks (f32/bf16/i8, harp_block_count elements), scales (fp32, one per
+    group, with int8 blocks only) and signs (d int8, or None)."""
+    if not isinstance(blocks, torch.Tensor) or blocks.dtype not in (torch.float32, torch.bfloat16, torch.int8):
+        raise TypeError(f"blocks{name} must be a float32, bfloat16 or int8 tensor")
+    _flat(blocks, "blocks" + name, blocks.dtype, harp_block_count(schedule, d))
+    if blocks.dtype == torch.int8:
+        if scales is None:
+            raise ValueError(f"int8 blocks{name} need scales{name}")
+        _flat(scales, "scales" + name, torch.float32, harp_group_count(schedule, d))
+    elif scales is not None:
+        raise ValueError(f"scales{name} go with int8 blocks only")
+    if signs is not None:
+        _flat(signs, "signs" + name, torch.int8, d)
+
+
 def _rows_ld(t, d, name):
     if t.dim() != 2 or t.shape[1] != d:
         raise ValueError(f"{name} must be 2-D with {d} columns, got {tuple(t.shape)}")
@@ -69,19 +100,21 @@ def harp_materialize_blocks(schedule, d: int, theta: torch.Tensor, gauss: torch.
                             scales_out: torch.Tensor | None = None, stream=None):
     """Blocks B = Q(theta) G for every stage and group (fp64 on device), stored
     as 'f32', 'bf16' or 'i8' (+ fp32 scales).  Returns (blocks, scales|None)."""
-    _dev(theta, "theta")
-    _dev(gauss, "gauss")
-    if theta.dtype != torch.float64 or (gauss is not None and gauss.dtype != torch.float64):
-        raise TypeError("theta and gauss must be float64")
-    if not theta.is_contiguous() or (gauss is not None and not gauss.is_contiguous()):
-        raise ValueError("theta and gauss must be contiguous")
+    _flat(theta, "theta", torch.float64, harp_theta_count(schedule, d))
+    if gauss is not None:
+        _flat(gauss, "gauss", torch.float64, harp_gauss_count(schedule, d))
     tdt = _BLK_NAME[block_dtype]
     if blocks_out is None:
         blocks_out = torch.empty(harp_block_count(schedule, d), dtype=tdt, device=theta.device)
     if block_dtype == "i8" and scales_out is None:
         scales_out = torch.empty(harp_group_count(schedule, d), dtype=torch.float32, device=theta.device)
-    _dev(blocks_out, "blocks_out")
-    _dev(scales_out, "scales_out")
+    _flat(blocks_out, "blocks_out", tdt, harp_block_count(schedule, d))
+    if block_dtype == "i8":
+        _flat(scales_out, "scales_out", torch.float32, harp_group_count(schedule, d))
+    elif scales_out is not None:
+        raise ValueError("scales_out goes with int8 blocks only")
+    for n, t in (("theta", theta), ("gauss", gauss), ("blocks_out", blocks_out), ("scales_out", scales_out)):
+        _dev(t, n)
     check(lib().harp_materialize_blocks(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta),
                                         _ptr(gauss), _DT[tdt],
                                         _ptr(blocks_out), _ptr(scales_out), _stream(stream)))
@@ -92,15 +125,15 @@ def harp_quantize_theta(schedule, d: int, theta: torch.Tensor, codes_out: torch.
                         scales_out: torch.Tensor | None = None, stream=None):
     """int8 codes and one fp32 scale per stage of fp64 theta, on device.
     Returns (codes, scales)."""
-    _dev(theta, "theta")
-    if theta.dtype != torch.float64 or not theta.is_contiguous():
-        raise TypeError("theta must be contiguous float64")
+    _flat(theta, "theta", torch.float64, harp_theta_count(schedule, d))
     if codes_out is None:
         codes_out = torch.empty(harp_theta_count(schedule, d), dtype=torch.int8, device=theta.device)
     if scales_out is None:
         scales_out = torch.empty(len(tuple(schedule)), dtype=torch.float32, device=theta.device)
-    _dev(codes_out, "codes_out")
-    _dev(scales_out, "scales_out")
+    _flat(codes_out, "codes_out", torch.int8, harp_theta_count(schedule, d))
+    _flat(scales_out, "scales_out", torch.float32, len(tuple(schedule)))
+    for n, t in (("theta", theta), ("codes_out", codes_out), ("scales_out", scales_out)):
+        _dev(t, n)
     check(lib().harp_quantize_theta(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta), _ptr(codes_out),
                                     _ptr(scales_out), _stream(stream)))
     return codes_out, scales_out
@@ -112,26 +145,23 @@ def harp_materialize_blocks_q8(schedule, d: int, theta_codes: torch.Tensor, thet
                                stream=None):
     """As harp_materialize_blocks, with theta given as int8 codes and one fp32
     scale per stage.  Returns (blocks, scales|None)."""
-    _dev(theta_codes, "theta_codes")
-    _dev(theta_scales, "theta_scales")
-    _dev(gauss, "gauss")
-    if theta_codes.dtype != torch.int8 or theta_scales.dtype != torch.float32:
-        raise TypeError("theta_codes must be int8 and theta_scales float32")
-    if gauss is not None and gauss.dtype != torch.float64:
-        raise TypeError("gauss must be float64")
-    if not theta_codes.is_contiguous() or not theta_scales.is_contiguous() or \
-            (gauss is not None and not gauss.is_contiguous()):
-        raise ValueError("theta_codes, theta_scales and gauss must be contiguous")
-    if theta_codes.numel() != harp_theta_count(schedule, d) or \
-            theta_scales.numel() != len(tuple(schedule)):
-        raise ValueError("theta_codes / theta_scales have the wrong length for this schedule")
+    _flat(theta_codes, "theta_codes", torch.int8, harp_theta_count(schedule, d))
+    _flat(theta_scales, "theta_scales", torch.float32, len(tuple(schedule)))
+    if gauss is not None:
+        _flat(gauss, "gauss", torch.float64, harp_gauss_count(schedule, d))
     tdt = _BLK_NAME[block_dtype]
     if blocks_out is None:
         blocks_out = torch.empty(harp_block_count(schedule, d), dtype=tdt, device=theta_codes.device)
     if block_dtype == "i8" and scales_out is None:
         scales_out = torch.empty(harp_group_count(schedule, d), dtype=torch.float32, device=theta_codes.device)
-    _dev(blocks_out, "blocks_out")
-    _dev(scales_out, "scales_out")
+    _flat(blocks_out, "blocks_out", tdt, harp_block_count(schedule, d))
+    if block_dtype == "i8":
+        _flat(scales_out, "scales_out", torch.float32, harp_group_count(schedule, d))
+    elif scales_out is not None:
+        raise ValueError("scales_out goes with int8 blocks only")
+    for n, t in (("theta_codes", theta_codes), ("theta_scales", theta_scales), ("gauss", gauss),
+                 ("blocks_out", blocks_out), ("scales_out", scales_out)):
+        _dev(t, n)
     check(lib().harp_materialize_blocks_q8(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta_codes),
                                            _ptr(theta_scales), _ptr(gauss), _DT[tdt], _ptr(blocks_out),
                                            _ptr(scales_out), _stream(stream)))
@@ -139,20 +169,29 @@ def harp_materialize_blocks_q8(schedule, d: int, theta_codes: torch.Tensor, thet
 
 
 # ------------------------------------------------------------------ apply
+# Every call below checks shapes, dtypes and sizes first and that every tensor
+# is on the GPU last, then calls the library once: nothing is launched for a
+# call that fails a check.
+
+def _out_like(out, x, d, name):
+    """The output of a row transform: x's row count and dtype (the library is
+    given one row count and one I/O dtype for both)."""
+    if out is None:
+        return torch.empty_like(x)
+    rows, _ = _rows_ld(out, d, name)
+    if rows != x.shape[0] or out.dtype != x.dtype:
+        raise ValueError(f"{name} must match the input in rows and dtype: {tuple(out.shape)} {out.dtype} "
+                         f"for {tuple(x.shape)} {x.dtype}")
+    return out
+
+
 def _apply(fn, schedule, d, blocks, scales, signs, x, y, stream):
-    _dev(blocks, "blocks")
-    _dev(scales, "scales")
-    _dev(signs, "signs")
-    _dev(x, "x")
+    _block_params(schedule, d, blocks, scales, signs)
     rows, ldx = _rows_ld(x, d, "x")
-    if y is None:
-        y = torch.empty_like(x)
-    _dev(y, "y")
-    rows_y, ldy = _rows_ld(y, d, "y")
-    if rows_y != rows or y.dtype != x.dtype:
-        raise ValueError("y must match x in rows and dtype")
-    if signs is not None and signs.dtype != torch.int8:
-        raise TypeError("signs must be int8")
+    y = _out_like(y, x, d, "y")
+    _, ldy = _rows_ld(y, d, "y")
+    for n, t in (("blocks", blocks), ("scales", scales), ("signs", signs), ("x", x), ("y", y)):
+        _dev(t, n)
     check(fn(ctypes.byref(Schedule.of(schedule)), d, _ptr(blocks), _DT[blocks.dtype], _ptr(scales),
              _ptr(signs), _ptr(x), ldx, _ptr(y), ldy, rows, _DT[x.dtype], _stream(stream)))
     return y
@@ -169,9 +208,17 @@ def harp_apply_inverse(schedule, d: int, blocks, scales, signs, y, x=None, strea
 
 
 def harp_apply_decode_workspace(schedule, d: int, block_dtype: str, rows: int) -> int:
-    """Workspace bytes harp_apply_decode needs (0: one launch, -1: unsupported)."""
+    """Workspace bytes harp_apply_decode needs (0: none, -1: unsupported)."""
     return int(lib().harp_apply_decode_workspace(ctypes.byref(Schedule.of(schedule)), d,
                                                  _DT[_BLK_NAME[block_dtype]], rows))
+
+
+def _workspace_bytes(workspace):
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    return workspace.numel() * workspace.element_size()
 
 
 def harp_apply_decode(schedule, d: int, blocks, scales, signs, x, y=None, inverse: bool = False,
@@ -179,26 +226,19 @@ def harp_apply_decode(schedule, d: int, blocks, scales, signs, x, y=None, invers
     """Small-batch apply (1 to a few hundred rows), forward or inverse.
     workspace: a device tensor of at least harp_apply_decode_workspace() bytes
     (allocated here when None and needed)."""
-    _dev(blocks, "blocks")
-    _dev(scales, "scales")
-    _dev(signs, "signs")
-    _dev(x, "x")
-    _dev(workspace, "workspace")
+    _block_params(schedule, d, blocks, scales, signs)
     rows, ldx = _rows_ld(x, d, "x")
-    if y is None:
-        y = torch.empty_like(x)
-    _dev(y, "y")
-    rows_y, ldy = _rows_ld(y, d, "y")
-    if rows_y != rows or y.dtype != x.dtype:
-        raise ValueError("y must match x in rows and dtype")
-    if signs is not None and signs.dtype != torch.int8:
-        raise TypeError("signs must be int8")
+    y = _out_like(y, x, d, "y")
+    _, ldy = _rows_ld(y, d, "y")
     sch = Schedule.of(schedule)
     if workspace is None:
         need = int(lib().harp_apply_decode_workspace(ctypes.byref(sch), d, _DT[blocks.dtype], rows))
         if need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _workspace_bytes(workspace)
+    for n, t in (("blocks", blocks), ("scales", scales), ("signs", signs), ("x", x), ("y", y),
+                 ("workspace", workspace)):
+        _dev(t, n)
     check(lib().harp_apply_decode(ctypes.byref(sch), d, _ptr(blocks), _DT[blocks.dtype], _ptr(scales),
                                   _ptr(signs), _ptr(x), ldx, _ptr(y), ldy, rows, _DT[x.dtype], int(inverse),
                                   _ptr(workspace), ws_bytes, _stream(stream)))
@@ -214,29 +254,29 @@ def harp_apply_vjp(schedule, d: int, blocks, scales, signs, x, dy, dx=None, want
                    dblocks=None, workspace=None, stream=None):
     """Reverse mode of harp_apply for an upstream gradient dy: returns
     (dx or None, dblocks), dblocks fp32 in the block layout."""
-    for n, t in (("blocks", blocks), ("scales", scales), ("signs", signs), ("x", x), ("dy", dy),
-                 ("dx", dx), ("dblocks", dblocks), ("workspace", workspace)):
-        _dev(t, n)
+    _block_params(schedule, d, blocks, scales, signs)
     rows, ldx = _rows_ld(x, d, "x")
-    rows_g, lddy = _rows_ld(dy, d, "dy")
-    if rows_g != rows or dy.dtype != x.dtype:
-        raise ValueError("dy must match x in rows and dtype")
-    if signs is not None and signs.dtype != torch.int8:
-        raise TypeError("signs must be int8")
+    if dy is None:
+        raise ValueError("dy is required")
+    dy = _out_like(dy, x, d, "dy")
+    _, lddy = _rows_ld(dy, d, "dy")
     if dx is None and want_dx:
         dx = torch.empty_like(x)
     lddx = 0
     if dx is not None:
-        rows_d, lddx = _rows_ld(dx, d, "dx")
-        if rows_d != rows or dx.dtype != x.dtype:
-            raise ValueError("dx must match x in rows and dtype")
+        dx = _out_like(dx, x, d, "dx")
+        _, lddx = _rows_ld(dx, d, "dx")
     if dblocks is None:
         dblocks = torch.empty(harp_block_count(schedule, d), dtype=torch.float32, device=x.device)
+    _flat(dblocks, "dblocks", torch.float32, harp_block_count(schedule, d))
     sch = Schedule.of(schedule)
     if workspace is None:
         need = int(lib().harp_apply_vjp_workspace(ctypes.byref(sch), d, rows))
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _workspace_bytes(workspace)
+    for n, t in (("blocks", blocks), ("scales", scales), ("signs", signs), ("x", x), ("dy", dy),
+                 ("dx", dx), ("dblocks", dblocks), ("workspace", workspace)):
+        _dev(t, n)
     check(lib().harp_apply_vjp(ctypes.byref(sch), d, _ptr(blocks), _DT[blocks.dtype], _ptr(scales), _ptr(signs),
                                _ptr(x), ldx, _ptr(dy), lddy, _ptr(dx), lddx, rows, _DT[x.dtype], _ptr(dblocks),
                                _ptr(workspace), ws_bytes, _stream(stream)))
@@ -245,34 +285,52 @@ def harp_apply_vjp(schedule, d: int, blocks, scales, signs, x, dy, dx=None, want
 
 def harp_theta_vjp(schedule, d: int, theta: torch.Tensor, gauss, dblocks, dtheta=None, stream=None):
     """dL/dtheta (fp64, theta's layout) from dL/dB (fp32 block layout)."""
-    for n, t in (("theta", theta), ("gauss", gauss), ("dblocks", dblocks), ("dtheta", dtheta)):
-        _dev(t, n)
-    if theta.dtype != torch.float64 or (gauss is not None and gauss.dtype != torch.float64):
-        raise TypeError("theta and gauss must be float64")
-    if dblocks.dtype != torch.float32 or dblocks.numel() != harp_block_count(schedule, d):
-        raise ValueError("dblocks must be float32 with harp_block_count() elements")
+    _flat(theta, "theta", torch.float64, harp_theta_count(schedule, d))
+    if gauss is not None:
+        _flat(gauss, "gauss", torch.float64, harp_gauss_count(schedule, d))
+    _flat(dblocks, "dblocks", torch.float32, harp_block_count(schedule, d))
     if dtheta is None:
         dtheta = torch.empty_like(theta)
+    _flat(dtheta, "dtheta", torch.float64, harp_theta_count(schedule, d))
+    for n, t in (("theta", theta), ("gauss", gauss), ("dblocks", dblocks), ("dtheta", dtheta)):
+        _dev(t, n)
     check(lib().harp_theta_vjp(ctypes.byref(Schedule.of(schedule)), d, _ptr(theta), _ptr(gauss), _ptr(dblocks),
                                _ptr(dtheta), _stream(stream)))
     return dtheta
 
 
 def harp_rotate_weight(su, blocks_u, scales_u, signs_u, sv, blocks_v, scales_v, signs_v, w,
-                       w_out=None, inverse: bool = False, workspace=None, stream=None):
-    """W_out = M_U W M_V^T (inverse: M_U^T W M_V); W is prod(su) x prod(sv)."""
-    for n, t in (("blocks_u", blocks_u), ("blocks_v", blocks_v), ("scales_u", scales_u), ("scales_v", scales_v),
-                 ("signs_u", signs_u), ("signs_v", signs_v), ("w", w), ("workspace", workspace)):
-        _dev(t, n)
+                       w_out=None, inverse: bool = False, workspace=None, fp32_intermediates: bool = True,
+                       stream=None):
+    """W_out = M_U W M_V^T (inverse: M_U^T W M_V); W is prod(su) x prod(sv).
+
+    Between its passes the rotation keeps the intermediate weight in fp32 in a
+    workspace (allocated here when none is given).  fp32_intermediates=False
+    with no workspace keeps it in W's dtype instead (no extra memory; for bf16
+    W, three roundings in place of one)."""
+    if w.dim() != 2:
+        raise ValueError(f"w must be 2-D, got {tuple(w.shape)}")
+    d_out, d_in = w.shape
+    _block_params(su, d_out, blocks_u, scales_u, signs_u, "_u")
+    _block_params(sv, d_in, blocks_v, scales_v, signs_v, "_v")
     if blocks_u.dtype != blocks_v.dtype:
         raise TypeError("blocks_u and blocks_v must share a dtype")
-    d_out, d_in = w.shape
     _, ldw = _rows_ld(w, d_in, "w")
     if w_out is None:
         w_out = torch.empty_like(w)
-    _dev(w_out, "w_out")
+    if tuple(w_out.shape) != tuple(w.shape) or w_out.dtype != w.dtype:
+        raise ValueError(f"w_out must match w in shape and dtype: {tuple(w_out.shape)} {w_out.dtype} "
+                         f"for {tuple(w.shape)} {w.dtype}")
     _, ldo = _rows_ld(w_out, d_in, "w_out")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None and fp32_intermediates:
+        need = harp_rotate_weight_workspace(d_out, d_in)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    ws_bytes = _workspace_bytes(workspace)
+    for n, t in (("blocks_u", blocks_u), ("blocks_v", blocks_v), ("scales_u", scales_u), ("scales_v", scales_v),
+                 ("signs_u", signs_u), ("signs_v", signs_v), ("w", w), ("w_out", w_out),
+                 ("workspace", workspace)):
+        _dev(t, n)
     check(lib().harp_rotate_weight(
         ctypes.byref(Schedule.of(su)), _ptr(blocks_u), _ptr(scales_u), _ptr(signs_u),
         ctypes.byref(Schedule.of(sv)), _ptr(blocks_v), _ptr(scales_v), _ptr(signs_v),
@@ -283,15 +341,14 @@ def harp_rotate_weight(su, blocks_u, scales_u, signs_u, sv, blocks_v, scales_v, 
 
 def rht_compose(schedule, d: int, signs, x, y=None, inverse: bool = False, stream=None):
     """y = (H D_k) ... (H D_1) x (inverse: (D_1 H) ... (D_k H) x); signs: k x d int8."""
-    _dev(signs, "signs")
-    _dev(x, "x")
-    if signs.dtype != torch.int8 or signs.dim() != 2 or signs.shape[1] != d or not signs.is_contiguous():
+    if not isinstance(signs, torch.Tensor) or signs.dtype != torch.int8 or signs.dim() != 2 or \
+            signs.shape[1] != d or not signs.is_contiguous():
         raise ValueError("signs must be a contiguous int8 tensor of shape (k, d)")
     rows, ldx = _rows_ld(x, d, "x")
-    if y is None:
-        y = torch.empty_like(x)
-    _dev(y, "y")
+    y = _out_like(y, x, d, "y")
     _, ldy = _rows_ld(y, d, "y")
+    for n, t in (("signs", signs), ("x", x), ("y", y)):
+        _dev(t, n)
     check(lib().rht_compose(ctypes.byref(Schedule.of(schedule)), d, _ptr(signs), signs.shape[0],
                             _ptr(x), ldx, _ptr(y), ldy, rows, _DT[x.dtype], int(bool(inverse)), _stream(stream)))
     return y

@@ -70,19 +70,34 @@ def _run(cmd: list[str]) -> None:
         print(out)
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """True if obj is missing or older than its source or any header it may
+    include (every header under csrc/ and include/ counts)."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    return any(os.path.getmtime(f) > t for f in deps)
+
+
+def build(jobs: int = 8, verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source (incremental=True: only those whose object is
+    stale) and link libharp.so."""
     os.makedirs(BUILD, exist_ok=True)
     steps = []
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        steps.append([HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        if not incremental or _stale(os.path.join(CSRC, src), obj):
+            steps.append([HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     cxx = shutil.which("g++") or "c++"
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        steps.append([cxx, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        if not incremental or _stale(os.path.join(CSRC, src), obj):
+            steps.append([cxx, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(_run, steps))
     tmp = LIB + ".tmp"
@@ -96,8 +111,10 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--incremental", action="store_true",
+                    help="recompile only sources whose object is older than the source or a header")
     args = ap.parse_args()
-    build(args.jobs)
+    build(args.jobs, incremental=args.incremental)
     return 0
 
 

@@ -271,7 +271,7 @@ harp_status harp_rotate_weight(const harp_schedule* su, const void* blocks_u, co
   if (!err.empty()) return fail(HARP_ERR_INVALID_ARG, err);
   if (workspace != nullptr) {
     if (workspace_bytes < harp_rotate_weight_workspace(d_out, d_in))
-      return fail(HARP_ERR_UNSUPPORTED, "workspace smaller than harp_rotate_weight_workspace()");
+      return fail(HARP_ERR_INVALID_ARG, "workspace smaller than harp_rotate_weight_workspace()");
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(HARP_ERR_INVALID_ARG, "workspace not 16-byte aligned");
   }
   const DT io = static_cast<DT>(io_dtype);

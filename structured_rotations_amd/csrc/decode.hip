@@ -687,7 +687,9 @@ int64_t decode_workspace_bytes(const Plan& pl, DT bdt, int64_t rows) {
   const int n = plan_runs(pl, bdt, runs);
   if (n == 0) return -1;
   if (rows > (INT64_MAX / 4) / pl.d) return -1;   // size not representable
-  return n == 1 ? 0 : rows * pl.d * 4;
+  // one launch, or a call handed to the throughput row kernels: no hand-off
+  if (n == 1 || rows > kDecodeRowsMax) return 0;
+  return rows * pl.d * 4;
 }
 
 hipError_t launch_apply_decode(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,

@@ -47,3 +47,19 @@ def assert_rows_close(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, label: s
     worst = float(err.max()) if err.size else 0.0
     assert worst <= tol, f"{label}: max per-row relative l2 {worst:.3e} > {tol:.1e} (row {int(err.argmax())})"
     return worst
+
+
+def assert_groups_close(got_flat: np.ndarray, ref_blocks, schedule, tol: float, label: str = ""):
+    """Per-group relative l2 of a block-layout array (dL/dB) against the
+    oracle's per-stage blocks: every group's b x b block is compared on its
+    own, so one group's error cannot hide under the norm of the others."""
+    pos = 0
+    worst = 0.0
+    for t, b in enumerate(schedule):
+        ref = np.asarray(ref_blocks[t], dtype=np.float64).reshape(-1, b * b)
+        got = np.asarray(got_flat[pos:pos + ref.size], dtype=np.float64).reshape(-1, b * b)
+        pos += ref.size
+        worst = max(worst, float(O.row_rel_l2(got, ref).max()))
+    assert pos == np.size(got_flat), f"{label}: {np.size(got_flat)} values for {pos} block entries"
+    assert worst <= tol, f"{label}: worst per-group relative l2 {worst:.3e} > {tol:.1e}"
+    return worst

@@ -155,7 +155,8 @@ def test_rotate_weight_rejects_on_host(lib):
     assert call(din=41) == _lib.HARP_ERR_INVALID_ARG
     assert call(ldw=39) == _lib.HARP_ERR_INVALID_ARG
     assert call(bu=None) == _lib.HARP_ERR_INVALID_ARG
-    assert call(ws=ctypes.c_void_p(0x40000), wsb=100) == _lib.HARP_ERR_UNSUPPORTED
+    assert call(ws=ctypes.c_void_p(0x40000), wsb=100) == _lib.HARP_ERR_INVALID_ARG      # too small
+    assert call(ws=ctypes.c_void_p(0x40004), wsb=24 * 40 * 4) == _lib.HARP_ERR_INVALID_ARG  # misaligned
     assert lib.harp_rotate_weight_workspace(24, 40) == 24 * 40 * 4
     assert lib.harp_rotate_weight_workspace(0, 40) == 0
 
@@ -173,6 +174,10 @@ def test_decode_workspace_sizes_on_host(lib):
     assert ws(ctypes.byref(Schedule.of((8, 8, 8, 8))), 4096, _lib.HARP_F32, 3) == 3 * 4096 * 4
     assert ws(ctypes.byref(Schedule.of((8, 8, 8, 5, 2))), 5120, _lib.HARP_BF16, 64) == 64 * 5120 * 4
     assert ws(ctypes.byref(Schedule.of((8, 8))), 64, _lib.HARP_F32, 5) == 0      # one launch
+    # above 128 rows the call runs the throughput row kernels: no hand-off buffer
+    assert ws(ctypes.byref(Schedule.of((8, 8, 8, 8))), 4096, _lib.HARP_F32, 128) == 128 * 4096 * 4
+    assert ws(ctypes.byref(Schedule.of((8, 8, 8, 8))), 4096, _lib.HARP_F32, 129) == 0
+    assert ws(ctypes.byref(Schedule.of((8, 8, 8, 5, 2))), 5120, _lib.HARP_BF16, 1024) == 0
     assert ws(ctypes.byref(Schedule.of((8, 8))), 65, _lib.HARP_F32, 5) == -1     # not a factorisation
     assert ws(ctypes.byref(Schedule.of((8, 8))), 64, 7, 5) == -1                 # bad dtype
     # a size that does not fit in int64 is -1, not a wrapped number
@@ -201,6 +206,11 @@ def test_decode_rejects_on_host(lib):
         _lib.HARP_ERR_INVALID_ARG
     assert dec(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 2, 2, 0, FAKE, 1 << 20, None) == \
         _lib.HARP_ERR_UNSUPPORTED
+    # above 128 rows no workspace is needed: a NULL one passes the host checks
+    # (the call then fails only on an odd x, which no element size allows)
+    assert dec(s, 4096, FAKE, 0, None, None, ctypes.c_void_p(0x10001), 4096, FAKE2, 4096, 200, 1, 0, None, 0,
+               None) == _lib.HARP_ERR_INVALID_ARG
+    assert "aligned" in lib.harp_last_error().decode()
     # zero rows: no launch, OK
     assert dec(s, 4096, None, 0, None, None, None, 4096, None, 4096, 0, 1, 0, None, 0, None) == _lib.HARP_OK
 

@@ -338,7 +338,7 @@ def _rotate_round_trip(c, io, blk, ws, label):
     bv, sv_ = gpu_blocks(api, c["sv"], c["dv"], c["tv"], c["gv"], blk)
     wd = to_dev(c["w"], io)
     wt = api.harp_rotate_weight(c["su"], bu, su_, signs_dev(c["su_s"]), c["sv"], bv, sv_, signs_dev(c["sv_s"]),
-                                wd, workspace=ws)
+                                wd, workspace=ws, fp32_intermediates=ws is not None)
     torch.cuda.synchronize()
     obu = oracle_blocks(c["su"], c["du"], c["tu"], c["gu"], blk)
     obv = oracle_blocks(c["sv"], c["dv"], c["tv"], c["gv"], blk)
@@ -347,7 +347,8 @@ def _rotate_round_trip(c, io, blk, ws, label):
     assert_rows_close(from_dev(wt), ref, TOL[io], f"{label} forward")
     wtin = from_dev(wt)
     back = api.harp_rotate_weight(c["su"], bu, su_, signs_dev(c["su_s"]), c["sv"], bv, sv_,
-                                  signs_dev(c["sv_s"]), wt, inverse=True, workspace=ws)
+                                  signs_dev(c["sv_s"]), wt, inverse=True, workspace=ws,
+                                  fp32_intermediates=ws is not None)
     torch.cuda.synchronize()
     ref_b = O.rotate_weight(wtin, c["su"], obu, c["su_s"].astype(float), c["sv"], obv, c["sv_s"].astype(float),
                             inverse=True)
@@ -403,23 +404,36 @@ def test_rotate_weight_radix16_column_path(io):
         _rotate_round_trip(c, io, blk, None, f"two-sided radix 16 {blk}/{io}")
 
 
-def test_rotate_weight_full_size_sampled():
+@pytest.mark.parametrize("fp32_intermediates", [True, False])
+def test_rotate_weight_full_size_sampled(fp32_intermediates):
+    # 13824 x 5120 bf16, U (8,8,8,3,3,3), V (8,8,8,5,2): the radix-8 column run
+    # (panel 64) and the radix-3 run (panel 512, 16-byte path) in both
+    # directions, against the oracle on sampled columns; intermediates in fp32
+    # (the binding's default workspace) or in bf16 in place
+    print(f"\n[case] two-sided full size, fp32 intermediates={fp32_intermediates}", flush=True)
     w = _case("two_sided_13824x5120_bf16")
     su, sv, du, dv = w["su"], w["schedule"], w["d_out"], w["d"]
     bu, _ = gpu_blocks(api, su, du, w["theta_u"], w["gauss_u"], "f32")
     bv, _ = gpu_blocks(api, sv, dv, w["theta_v"], w["gauss_v"], "f32")
+    sgu, sgv = signs_dev(w["signs_u"]), signs_dev(w["signs_v"])
     wd = to_dev(w["x"], "bf16")
-    wt = api.harp_rotate_weight(su, bu, None, signs_dev(w["signs_u"]), sv, bv, None, signs_dev(w["signs_v"]), wd)
-    back = api.harp_rotate_weight(su, bu, None, signs_dev(w["signs_u"]), sv, bv, None, signs_dev(w["signs_v"]),
-                                  wt, inverse=True)
+    wt = api.harp_rotate_weight(su, bu, None, sgu, sv, bv, None, sgv, wd, fp32_intermediates=fp32_intermediates)
+    back = api.harp_rotate_weight(su, bu, None, sgu, sv, bv, None, sgv, wt, inverse=True,
+                                  fp32_intermediates=fp32_intermediates)
     torch.cuda.synchronize()
-    # oracle on a sample of columns: V on every row, then U on the sampled columns
     obu = oracle_blocks(su, du, w["theta_u"], w["gauss_u"], "f32")
     obv = oracle_blocks(sv, dv, w["theta_v"], w["gauss_v"], "f32")
-    cols = np.sort(SAMPLE.choice(dv, 24, replace=False))
-    rowsv = O.apply(w["x"].astype(np.float64), sv, obv, w["signs_v"].astype(float))
-    ref_cols = O.apply(rowsv[:, cols].T, su, obu, w["signs_u"].astype(float))     # (24, du)
-    got_cols = from_dev(wt[:, torch.from_numpy(cols).cuda()]).T
-    assert_rows_close(got_cols, ref_cols, TOL["bf16"], "two-sided full (sampled columns)")
-    # round trip back to W
+    s_u, s_v = w["signs_u"].astype(float), w["signs_v"].astype(float)
+    cols = np.sort(SAMPLE.choice(dv, 64, replace=False))
+    tcols = torch.from_numpy(cols).cuda()
+    # forward: V on every row, then U on the sampled columns
+    rowsv = O.apply(w["x"].astype(np.float64), sv, obv, s_v)
+    ref_cols = O.apply(rowsv[:, cols].T, su, obu, s_u)                          # (64, du)
+    assert_rows_close(from_dev(wt[:, tcols]).T, ref_cols, TOL["bf16"], "two-sided full forward (sampled columns)")
+    # inverse of the GPU's own forward output: M_U^T W~ M_V, i.e. the inverse
+    # transform of V on every row, then of U on the sampled columns
+    rows_inv = O.apply_inverse(from_dev(wt), sv, obv, s_v)
+    ref_inv = O.apply_inverse(rows_inv[:, cols].T, su, obu, s_u)
+    assert_rows_close(from_dev(back[:, tcols]).T, ref_inv, TOL["bf16"], "two-sided full inverse (sampled columns)")
+    # and the round trip back to W
     assert_rows_close(from_dev(back[:64]), w["x"][:64].astype(np.float64), 2 * TOL["bf16"], "two-sided roundtrip")

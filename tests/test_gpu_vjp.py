@@ -17,7 +17,7 @@ from structured_rotations_amd import api
 from structured_rotations_amd import inputs as I
 from structured_rotations_amd import workloads as W
 from structured_rotations_amd._lib import HarpError
-from tests.parity_util import (TOL, assert_rows_close, from_dev, gpu_blocks, oracle_blocks, signs_dev, to_dev)
+from tests.parity_util import (TOL, assert_groups_close, assert_rows_close, from_dev, gpu_blocks, oracle_blocks, signs_dev, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,18 +29,6 @@ def _dy(rows, d, io, seed):
     if io == "bf16":
         g = torch.from_numpy(g).to(torch.bfloat16).float().numpy()
     return g
-
-
-def _assert_groups_close(got_flat, ref_blocks, sch, tol, label):
-    pos = 0
-    worst = 0.0
-    for t, b in enumerate(sch):
-        ref = ref_blocks[t].reshape(-1, b * b)
-        got = got_flat[pos:pos + ref.size].reshape(-1, b * b)
-        pos += ref.size
-        err = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
-        worst = max(worst, float(err.max()))
-    assert worst <= tol, f"{label}: worst per-group relative l2 {worst:.3e} > {tol:.1e}"
 
 
 @pytest.mark.parametrize("name", ["sylvester64_f32", "cayley4096_bf16", "mixed5120_bf16"])
@@ -58,7 +46,7 @@ def test_vjp_matches_oracle(name, blk):
     blocks_o = oracle_blocks(sch, d, w["theta"], w["gauss"], blk)
     rdx, rdb = O.apply_vjp(w["x"].astype(np.float64), sch, blocks_o, w["signs"].astype(float), dy.astype(np.float64))
     assert_rows_close(from_dev(dx), rdx, TOL[io], f"{name}/{blk} dx")
-    _assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, f"{name}/{blk} dB")
+    assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, f"{name}/{blk} dB")
 
 
 @pytest.mark.parametrize("sch,d", [((8, 8, 8, 3, 3, 3), 13824), ((2, 5, 4), 40), ((7,), 7), ((3, 2, 6), 36)])
@@ -77,7 +65,7 @@ def test_vjp_other_schedules(sch, d):
     blocks_o = oracle_blocks(sch, d, theta, gauss, "f32")
     rdx, rdb = O.apply_vjp(x.astype(np.float64), sch, blocks_o, signs.astype(float), dy.astype(np.float64))
     assert_rows_close(from_dev(dx), rdx, TOL["f32"], f"{sch} dx")
-    _assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, f"{sch} dB")
+    assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, f"{sch} dB")
 
 
 @pytest.mark.parametrize("name", ["cayley4096_bf16", "mixed5120_bf16"])
@@ -117,7 +105,7 @@ def test_vjp_full_chain_to_theta_at_calibration_size():
     torch.cuda.synchronize()
     blocks_o = oracle_blocks(sch, d, w["theta"], w["gauss"], "f32")
     _, rdb = O.apply_vjp(w["x"].astype(np.float64), sch, blocks_o, w["signs"].astype(float), dy.astype(np.float64))
-    _assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, "full dB")
+    assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, "full dB")
     rdt = O.theta_vjp(sch, d, w["theta"], w["gauss"], rdb)
     got = dt.cpu().numpy()
     pos = 0
@@ -155,4 +143,4 @@ def test_vjp_without_signs_and_one_row():
     blocks_o = oracle_blocks(sch, d, w["theta"], w["gauss"], "f32")
     rdx, rdb = O.apply_vjp(w["x"].astype(np.float64), sch, blocks_o, None, dy.astype(np.float64))
     assert_rows_close(from_dev(dx), rdx, TOL["f32"], "dx")
-    _assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, "dB")
+    assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, "dB")

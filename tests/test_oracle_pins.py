@@ -646,3 +646,28 @@ def test_rht_one_hot_marginals_diagnostic():
         dist[k] = scipy.stats.kstest(z.ravel(), "norm").statistic
     print(f"Kolmogorov distance to N(0,1): k=2 {dist[2]:.4f}, k=3 {dist[3]:.4f}")
     assert dist[2] < 0.02 and dist[3] < 0.02
+
+
+# ---------------------------------------------------------------- parity metric
+def test_row_rel_l2_hand_example():
+    # The per-row relative l2 error every parity bound is stated for, against
+    # values worked out by hand (tests/golden/row_rel_l2_hand.json): a divisor
+    # of ||y|| instead of ||ref||, a sum instead of a difference, a squared
+    # ratio, a max over columns, a zero reference row or one global ratio over
+    # the batch would each give other numbers.
+    with open(os.path.join(GOLDEN, "row_rel_l2_hand.json")) as f:
+        fx = json.load(f)
+    got = O.row_rel_l2(np.array(fx["y"], dtype=float), np.array(fx["ref"], dtype=float))
+    assert got.shape == (len(fx["ref"]),)
+    np.testing.assert_allclose(got, fx["per_row"], rtol=1e-15, atol=0)
+
+
+def test_row_rel_l2_scale_and_single_row():
+    # Invariants that need no arithmetic of the metric: a common factor on both
+    # arguments leaves it unchanged, equal rows give exactly zero, and a 1-D row
+    # is treated as one row.
+    y = np.array([[1.0, -2.0, 0.5], [0.0, 3.0, 4.0]])
+    ref = np.array([[1.0, -2.5, 0.0], [0.0, 3.0, 4.0]])
+    np.testing.assert_allclose(O.row_rel_l2(7.0 * y, 7.0 * ref), O.row_rel_l2(y, ref), rtol=1e-15)
+    assert O.row_rel_l2(ref, ref).tolist() == [0.0, 0.0]
+    assert O.row_rel_l2(y[0], ref[0]).shape == (1,)
