@@ -14,7 +14,8 @@ import torch
 from oracle import harp_oracle as O
 from structured_rotations_amd import api
 from structured_rotations_amd import workloads as W
-from tests.parity_util import (TOL, assert_rows_close, from_dev, gpu_blocks, oracle_blocks, signs_dev, to_dev)
+from tests.parity_util import (TOL, TOL_BF16_THREE_ROUNDINGS, assert_rows_close, from_dev, gpu_blocks, oracle_blocks,
+                               signs_dev, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -344,7 +345,9 @@ def _rotate_round_trip(c, io, blk, ws, label):
     obv = oracle_blocks(c["sv"], c["dv"], c["tv"], c["gv"], blk)
     ref = O.rotate_weight(c["w"].astype(float), c["su"], obu, c["su_s"].astype(float), c["sv"], obv,
                           c["sv_s"].astype(float))
-    assert_rows_close(from_dev(wt), ref, TOL[io], f"{label} forward")
+    # without a workspace a bf16 weight is rounded between the passes
+    tol = TOL_BF16_THREE_ROUNDINGS if (io == "bf16" and ws is None) else TOL[io]
+    assert_rows_close(from_dev(wt), ref, tol, f"{label} forward")
     wtin = from_dev(wt)
     back = api.harp_rotate_weight(c["su"], bu, su_, signs_dev(c["su_s"]), c["sv"], bv, sv_,
                                   signs_dev(c["sv_s"]), wt, inverse=True, workspace=ws,
@@ -352,7 +355,7 @@ def _rotate_round_trip(c, io, blk, ws, label):
     torch.cuda.synchronize()
     ref_b = O.rotate_weight(wtin, c["su"], obu, c["su_s"].astype(float), c["sv"], obv, c["sv_s"].astype(float),
                             inverse=True)
-    assert_rows_close(from_dev(back), ref_b, TOL[io], f"{label} inverse")
+    assert_rows_close(from_dev(back), ref_b, tol, f"{label} inverse")
 
 
 @pytest.mark.parametrize("use_ws", [False, True])
@@ -429,11 +432,12 @@ def test_rotate_weight_full_size_sampled(fp32_intermediates):
     # forward: V on every row, then U on the sampled columns
     rowsv = O.apply(w["x"].astype(np.float64), sv, obv, s_v)
     ref_cols = O.apply(rowsv[:, cols].T, su, obu, s_u)                          # (64, du)
-    assert_rows_close(from_dev(wt[:, tcols]).T, ref_cols, TOL["bf16"], "two-sided full forward (sampled columns)")
+    tol = TOL["bf16"] if fp32_intermediates else TOL_BF16_THREE_ROUNDINGS
+    assert_rows_close(from_dev(wt[:, tcols]).T, ref_cols, tol, "two-sided full forward (sampled columns)")
     # inverse of the GPU's own forward output: M_U^T W~ M_V, i.e. the inverse
     # transform of V on every row, then of U on the sampled columns
     rows_inv = O.apply_inverse(from_dev(wt), sv, obv, s_v)
     ref_inv = O.apply_inverse(rows_inv[:, cols].T, su, obu, s_u)
-    assert_rows_close(from_dev(back[:, tcols]).T, ref_inv, TOL["bf16"], "two-sided full inverse (sampled columns)")
+    assert_rows_close(from_dev(back[:, tcols]).T, ref_inv, tol, "two-sided full inverse (sampled columns)")
     # and the round trip back to W
-    assert_rows_close(from_dev(back[:64]), w["x"][:64].astype(np.float64), 2 * TOL["bf16"], "two-sided roundtrip")
+    assert_rows_close(from_dev(back[:64]), w["x"][:64].astype(np.float64), 2 * tol, "two-sided roundtrip")
