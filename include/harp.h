@@ -217,6 +217,37 @@ harp_status harp_apply_decode(const harp_schedule* s, int64_t d,
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Small-batch apply that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.
+ *
+ * Computes exactly what harp_apply_decode computes, with the same kernels,
+ * arguments, layouts and errors, except that the fp32 hand-off between its
+ * two launches lives in a buffer inside the library: a file-scope device
+ * array of HARP_NOALLOC_SCRATCH_BYTES per GPU (each GPU the library runs on
+ * holds its own copy until the process ends).  Its address is looked up once
+ * per device, on the first call with that device current; the call uses the
+ * calling thread's current device, which must be the device of `stream`.
+ * No hipMalloc, hipFree or other allocating routine is called.
+ * A call needing more than HARP_NOALLOC_SCRATCH_BYTES (rows * d * 4 bytes
+ * for a two-launch schedule at up to 128 rows: e.g. 512 rows of d = 4096 is
+ * handed to the row kernels and needs none, 128 rows of d = 16384 needs all
+ * 8 MiB) returns HARP_ERR_INVALID_ARG without a launch.
+ * Every call on one GPU shares that GPU's buffer and leaves the last call's
+ * rows in it; nothing in it needs to start at zero (the first launch writes
+ * every element the second one reads).  Calls that overlap in time on one
+ * GPU (different streams, or host threads without ordering) race on it and
+ * must not be issued.
+ * ---------------------------------------------------------------------- */
+#define HARP_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+harp_status harp_apply_decode_noalloc(const harp_schedule* s, int64_t d,
+                                      const void* blocks, harp_dtype block_dtype,
+                                      const float* block_scales, const int8_t* signs,
+                                      const void* x, int64_t ldx, void* y, int64_t ldy,
+                                      int64_t rows, harp_dtype io_dtype, int32_t inverse,
+                                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Reverse mode, for fitting the parameters on calibration data   [TS §2.3:
  * the parameters are fitted per layer by minimising a calibration loss;
  * TS §2.1-§2.2 for the transform being differentiated]

@@ -21,6 +21,7 @@ HARP_I8 = 2
 HARP_F64 = 3
 
 MAX_STAGES = 16
+NOALLOC_SCRATCH_BYTES = 8 << 20      # HARP_NOALLOC_SCRATCH_BYTES
 
 
 class Schedule(ctypes.Structure):
@@ -76,6 +77,8 @@ _SIG = {
     "harp_apply_decode_workspace": (_I64, [ctypes.POINTER(Schedule), _I64, _I32, _I64]),
     "harp_apply_decode": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64, _I64, _I32,
                                  _I32, _P, ctypes.c_size_t, _P]),
+    "harp_apply_decode_noalloc": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _P, _P, _I64, _P, _I64,
+                                         _I64, _I32, _I32, _P]),
     "harp_rotate_weight": (_I32, [ctypes.POINTER(Schedule), _P, _P, _P, ctypes.POINTER(Schedule), _P, _P, _P,
                                   _I32, _P, _I64, _P, _I64, _I64, _I64, _I32, _I32, _P, ctypes.c_size_t, _P]),
     "rht_compose": (_I32, [ctypes.POINTER(Schedule), _I64, _P, _I32, _P, _I64, _P, _I64, _I64, _I32, _I32, _P]),

@@ -245,6 +245,24 @@ def harp_apply_decode(schedule, d: int, blocks, scales, signs, x, y=None, invers
     return y
 
 
+def harp_apply_decode_noalloc(schedule, d: int, blocks, scales, signs, x, y, inverse: bool = False, stream=None):
+    """harp_apply_decode with its hand-off rows in the library's own per-GPU
+    buffer: allocates nothing (y must be given).  Calls that overlap in time
+    on one GPU must not be issued (they share the buffer)."""
+    _block_params(schedule, d, blocks, scales, signs)
+    rows, ldx = _rows_ld(x, d, "x")
+    if y is None:
+        raise ValueError("y is required (this entry point allocates nothing)")
+    y = _out_like(y, x, d, "y")
+    _, ldy = _rows_ld(y, d, "y")
+    for n, t in (("blocks", blocks), ("scales", scales), ("signs", signs), ("x", x), ("y", y)):
+        _dev(t, n)
+    check(lib().harp_apply_decode_noalloc(ctypes.byref(Schedule.of(schedule)), d, _ptr(blocks), _DT[blocks.dtype],
+                                          _ptr(scales), _ptr(signs), _ptr(x), ldx, _ptr(y), ldy, rows,
+                                          _DT[x.dtype], int(inverse), _stream(stream)))
+    return y
+
+
 def harp_apply_vjp_workspace(schedule, d: int, rows: int) -> int:
     """Workspace bytes harp_apply_vjp needs (-1: a radix above 8)."""
     return int(lib().harp_apply_vjp_workspace(ctypes.byref(Schedule.of(schedule)), d, rows))

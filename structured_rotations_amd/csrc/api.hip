@@ -1,6 +1,7 @@
 // extern "C" entry points declared in include/harp.h: argument validation on
 // the host (before any HIP call), then the kernel launchers.
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "harp.h"
@@ -173,6 +174,80 @@ harp_status harp_apply_decode(const harp_schedule* s, int64_t d, const void* blo
                                                  signs, x, ldx, io, y, ldy, rows, static_cast<float*>(workspace),
                                                  stream),
                        "harp_apply_decode");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------
+// Hand-off buffer of harp_apply_decode_noalloc: the fp32 rows passed from the
+// first launch to the second.  Each GPU the library runs on holds its own
+// copy until the process ends.  Host code never uses the array's name as an
+// address (it is a host-side stand-in); it uses the device address obtained
+// once per device with hipGetSymbolAddress, with that device current.
+namespace {
+
+static __device__ __align__(256) float scratch[HARP_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of `scratch`.
+harp_status device_scratch(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HARP_ERR_LAUNCH, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HARP_ERR_UNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || p == nullptr)
+      return fail(HARP_ERR_LAUNCH, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(es));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HARP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+harp_status harp_apply_decode_noalloc(const harp_schedule* s, int64_t d, const void* blocks, harp_dtype block_dtype,
+                                      const float* block_scales, const int8_t* signs, const void* x, int64_t ldx,
+                                      void* y, int64_t ldy, int64_t rows, harp_dtype io_dtype, int32_t inverse,
+                                      hipStream_t stream) {
+  Plan pl;
+  std::string err;
+  if (!plan_of(s, d, &pl, &err)) return fail(HARP_ERR_INVALID_ARG, err);
+  if (!io_ok(io_dtype)) return fail(HARP_ERR_UNSUPPORTED, "io_dtype must be HARP_F32 or HARP_BF16");
+  if (!blk_ok(block_dtype)) return fail(HARP_ERR_UNSUPPORTED, "block_dtype must be HARP_F32, HARP_BF16 or HARP_I8");
+  if ((block_dtype == HARP_I8) != (block_scales != nullptr))
+    return fail(HARP_ERR_INVALID_ARG, "block_scales must be given exactly for HARP_I8 blocks");
+  if (rows > HARP_DECODE_MAX_ROWS)
+    return fail(HARP_ERR_INVALID_ARG,
+                "harp_apply_decode_noalloc takes at most HARP_DECODE_MAX_ROWS rows; use harp_apply");
+  const int eb = io_dtype == HARP_F32 ? 4 : 2;
+  err = harp::check_rows(x, ldx, y, ldy, rows, d, eb);
+  if (!err.empty()) return fail(HARP_ERR_INVALID_ARG, err);
+  const int64_t need = harp::decode_workspace_bytes(pl, static_cast<DT>(block_dtype), rows);
+  if (need < 0) return fail(HARP_ERR_UNSUPPORTED, "no split of this schedule into two digit runs fits a workgroup");
+  if (need > (int64_t)HARP_NOALLOC_SCRATCH_BYTES)
+    return fail(HARP_ERR_INVALID_ARG,
+                "rows * d * 4 exceeds HARP_NOALLOC_SCRATCH_BYTES; use harp_apply_decode with a workspace");
+  if (rows == 0) return HARP_OK;
+  if (blocks == nullptr) return fail(HARP_ERR_INVALID_ARG, "blocks is NULL");
+  void* ws = nullptr;
+  if (need > 0) {
+    const harp_status st = device_scratch(&ws);
+    if (st != HARP_OK) return st;
+  }
+  const DT io = static_cast<DT>(io_dtype);
+  return launch_status(harp::launch_apply_decode(pl, inverse != 0, blocks, static_cast<DT>(block_dtype), block_scales,
+                                                 signs, x, ldx, io, y, ldy, rows, static_cast<float*>(ws), stream),
+                       "harp_apply_decode_noalloc");
 }
 
 int64_t harp_apply_vjp_workspace(const harp_schedule* s, int64_t d, int64_t rows) {

@@ -239,3 +239,17 @@ def test_vjp_rejects_on_host(lib):
     assert tv(s, 4096, FAKE, None, None, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
     assert tv(s, 4096, FAKE, None, FAKE, None, None) == _lib.HARP_ERR_INVALID_ARG
     assert tv(ctypes.byref(Schedule.of((8, 5))), 40, FAKE, None, FAKE, FAKE2, None) == _lib.HARP_ERR_INVALID_ARG
+
+
+def test_decode_noalloc_rejects_on_host(lib):
+    na = lib.harp_apply_decode_noalloc
+    s = ctypes.byref(Schedule.of((8, 8, 8, 8)))
+    assert na(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 1025, 1, 0, None) == _lib.HARP_ERR_INVALID_ARG
+    assert na(s, 4096, FAKE, 2, None, None, FAKE, 4096, FAKE2, 4096, 2, 1, 0, None) == _lib.HARP_ERR_INVALID_ARG
+    assert na(s, 4096, FAKE, 0, None, None, FAKE, 4096, FAKE2, 4096, 2, 2, 0, None) == _lib.HARP_ERR_UNSUPPORTED
+    # 128 rows of d = 32768 need 16 MiB of hand-off rows, beyond the 8 MiB buffer
+    s5 = ctypes.byref(Schedule.of((8, 8, 8, 8, 8)))
+    big = ctypes.c_void_p(1 << 40)
+    assert na(s5, 32768, FAKE, 0, None, None, big, 32768, big, 32768, 128, 1, 0, None) == _lib.HARP_ERR_INVALID_ARG
+    assert "HARP_NOALLOC_SCRATCH_BYTES" in lib.harp_last_error().decode()
+    assert na(s, 4096, None, 0, None, None, None, 4096, None, 4096, 0, 1, 0, None) == _lib.HARP_OK
