@@ -108,12 +108,29 @@ def build(jobs: int = 8, verbose: bool = True, incremental: bool = False) -> str
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "hwprobe.hip")
+PROBE = os.path.join(PKG, "hwprobe")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Compile the device-rate probe (a standalone gfx950 program)."""
+    _run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+          "-packed-fp32-ops", PROBE_SRC, "-o", PROBE])
+    if verbose:
+        print(f"built {PROBE}")
+    return PROBE
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--incremental", action="store_true",
                     help="recompile only sources whose object is older than the source or a header")
+    ap.add_argument("--probe", action="store_true", help="build the device-rate probe instead of the library")
     args = ap.parse_args()
+    if args.probe:
+        build_probe()
+        return 0
     build(args.jobs, incremental=args.incremental)
     return 0
 

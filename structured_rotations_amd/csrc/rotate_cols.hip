@@ -42,6 +42,8 @@ struct ColParams {
   int vec;           // 16-byte row segments and whole panels: aligned bases, ld and widths
   int dup;           // chunk slots wrap around (some chunks have two owners)
   uint32_t mag_ncb;  // ceil(2^32 / (pw / 64)) (0 for one block)
+  uint32_t mag_cpr;  // same for the input chunks per tile row, pw / (16 / input element bytes)
+  uint32_t mag_tot;  // same for the input chunks per tile, nsub * pw / (16 / input element bytes)
   ColStage st[kMaxStagesDev];
   const void* blocks;
   const float* scales;
@@ -300,9 +302,9 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* v, float*) {
 // and stores per tile and the waits before a prefetched tile goes into LDS
 // count them exactly.  With fewer than 512 chunks a thread may have no chunk
 // of its own: then the slot wraps to another thread's chunk (p.dup).
-__device__ __forceinline__ int chunk_of(int j, int total) {
+__device__ __forceinline__ int chunk_of(int j, int total, uint32_t mag_tot) {
   const int i = (int)threadIdx.x + j * 512;
-  return i < total ? i : (total >= 512 ? (int)threadIdx.x : i % total);
+  return i < total ? i : (total >= 512 ? (int)threadIdx.x : i - udiv(i, mag_tot) * total);
 }
 
 // The D_s factor of the pass (sign_mode 1: on the rows as they enter the
@@ -318,8 +320,8 @@ __device__ __forceinline__ void col_prefetch(const ColParams& p, const ColTile& 
   const int total = p.nsub * cpr;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
-    const int i = chunk_of(j, total);
-    const int u = i / cpr;
+    const int i = chunk_of(j, total, p.mag_tot);
+    const int u = udiv(i, p.mag_cpr);
     const int ch = i - u * cpr;
     const int64_t row = t.row_base + (int64_t)u * p.suf;
     r[j] = ld_stream(x + row * p.ldx + t.col0 + ch * VI);
@@ -351,9 +353,9 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
   uint32_t nmask = 0;
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
-    const int i = chunk_of(j, total);
+    const int i = chunk_of(j, total, p.mag_tot);
     const bool rep = j > 0 && total >= 512 && (int)threadIdx.x + j * 512 >= total;
-    const int u = i / cpr_i;
+    const int u = udiv(i, p.mag_cpr);
     const int ch = i - u * cpr_i;
     float* loc = tile + u * p.pw + ch * VI;
     if (has_done) {
@@ -648,6 +650,12 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   if (pw_div > 0) pw = pw_div;
   p.pw = pw;
   p.mag_ncb = mag(pw / 64);
+  {
+    // input chunks per tile row and per tile (below 2^16: the tile is at most 160 KiB of fp32)
+    const int vin = 16 / io_bytes(in_dt);
+    p.mag_cpr = mag(pw / vin);
+    p.mag_tot = mag(nsub * (pw / vin));
+  }
   p.ncols = ncols;
   p.npanels = (ncols + pw - 1) / pw;
   p.ntiles = (pl.d / nsub) * p.npanels;

@@ -1,12 +1,14 @@
 """Summaries of rocprofv3 output (SQLite result databases) for the kernels here.
 
     python -m structured_rotations_amd.profsum stats DB [--match SUBSTR]
+    python -m structured_rotations_amd.profsum by-kernel DB [--match SUBSTR]
     python -m structured_rotations_amd.profsum traffic --kernel SUBSTR \\
         --fetch DB --write DB --copy-fetch DB --copy-write DB --copy-bytes N \\
         --workload NAME --blk f32 --command "..." --out profiles/traffic_NAME_f32.json
 
 `stats` prints per-kernel launch counts and durations (and the per-dispatch
-average of every counter the database holds).  `traffic` turns two counter
+average of every counter the database holds, over all matching kernels);
+`by-kernel` prints those averages per kernel, one column each.  `traffic` turns two counter
 runs of a kernel (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) into HBM
 bytes per launch, each scaled by what the same counter reads for a plain
 device copy of known size, and records it with the hash of that kernel's sources
@@ -61,6 +63,32 @@ def counters(db: str, match: str):
     return {k: tot[k] / len(disp[k]) for k in tot}
 
 
+def counters_by_kernel(db: str, match: str):
+    """{kernel name: {counter: per-dispatch average}} for kernels containing `match`."""
+    con = sqlite3.connect(db)
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(lambda: collections.defaultdict(set))
+    for name, d, cn, cv in con.execute("select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if match in name:
+            tot[name][cn] += cv
+            disp[name][cn].add(d)
+    return {n: {k: tot[n][k] / len(disp[n][k]) for k in tot[n]} for n in tot}
+
+
+def cmd_by_kernel(args) -> int:
+    per = counters_by_kernel(args.db, args.match)
+    names = sorted(per)
+    cnames = sorted({c for n in names for c in per[n]})
+    for i, n in enumerate(names):
+        print(f"- k{i}: `{n}`")
+    print()
+    print("| counter | " + " | ".join(f"k{i}" for i in range(len(names))) + " |")
+    print("|---|" + "---|" * len(names))
+    for c in cnames:
+        print(f"| {c} | " + " | ".join(f"{per[n].get(c, float('nan')):,.0f}" for n in names) + " |")
+    return 0
+
+
 def cmd_stats(args) -> int:
     st = kernel_stats(args.db, args.match)
     print("| kernel | launches | mean us | min us | max us | grid (threads) | block | LDS B |")
@@ -104,6 +132,9 @@ def main(argv=None) -> int:
     s = sub.add_parser("stats")
     s.add_argument("db")
     s.add_argument("--match", default="")
+    k = sub.add_parser("by-kernel")
+    k.add_argument("db")
+    k.add_argument("--match", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-kernel", default="copyBuffer")
@@ -115,7 +146,7 @@ def main(argv=None) -> int:
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    return cmd_stats(args) if args.cmd == "stats" else cmd_traffic(args)
+    return {"stats": cmd_stats, "by-kernel": cmd_by_kernel, "traffic": cmd_traffic}[args.cmd](args)
 
 
 if __name__ == "__main__":
