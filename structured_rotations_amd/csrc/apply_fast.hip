@@ -97,7 +97,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coef_rsrc(const RowParams& p) 
 
 // cf[h][k] = C[4h + j][k] of group g0 + gb (C = B forward, B^T inverse; g0
 // uniform); lanes whose row 4h + j is past the radix re-read row B - 1 (their
-// outputs are dropped).
+// outputs are dropped).  Rows of bf16 blocks (forward) stay packed, two per
+// word, as they arrive: decode_coef widens them where the round uses them,
+// so no wait for the load lands where it is issued (bf16 blocks then move
+// half the bytes of fp32 at no extra stall).  The inverse reads columns one
+// element at a time and widens each at once (deferring those measured
+// slower).
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void load_coef(__amdgpu_buffer_rsrc_t rs, const StageFast& sd, int g0, int gb, int j,
                                           float (&cf)[2][8]) {
@@ -120,11 +125,11 @@ __device__ __forceinline__ void load_coef(__amdgpu_buffer_rsrc_t rs, const Stage
         }
       } else if constexpr (B == 8) {
         const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
-        cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
-        cf[h][4] = bf16_lo(a.z); cf[h][5] = bf16_hi(a.z); cf[h][6] = bf16_lo(a.w); cf[h][7] = bf16_hi(a.w);
+        cf[h][0] = __uint_as_float(a.x); cf[h][1] = __uint_as_float(a.y);
+        cf[h][2] = __uint_as_float(a.z); cf[h][3] = __uint_as_float(a.w);
       } else {
         const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
-        cf[h][0] = bf16_lo(a.x); cf[h][1] = bf16_hi(a.x); cf[h][2] = bf16_lo(a.y); cf[h][3] = bf16_hi(a.y);
+        cf[h][0] = __uint_as_float(a.x); cf[h][1] = __uint_as_float(a.y);
       }
     } else {
       // element (o, k) of C sits at k * B + o (transposed) or o * B + k
@@ -141,10 +146,31 @@ __device__ __forceinline__ void load_coef(__amdgpu_buffer_rsrc_t rs, const Stage
   }
 }
 
+// The fp32 coefficients of a buffer filled by load_coef.
+template <int B, typename TB, bool TR>
+__device__ __forceinline__ void decode_coef(const float (&raw)[2][8], float (&cf)[2][8]) {
+  constexpr int NH = B > 4 ? 2 : 1;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    if constexpr (!std::is_same<TB, float>::value && !TR && (B == 8 || B == 4)) {
+#pragma unroll
+      for (int i = 0; i < B / 2; ++i) {
+        cf[h][2 * i] = bf16_lo(__float_as_uint(raw[h][i]));
+        cf[h][2 * i + 1] = bf16_hi(__float_as_uint(raw[h][i]));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < B; ++k) cf[h][k] = raw[h][k];
+    }
+  }
+}
+
 // One round: 16 groups per compute wave, both row quads.
-template <class Sch, int B, int S, bool TR, bool DIRECT, typename T>
-__device__ __forceinline__ void round_compute(const RowParams& p, float* tile, int g, const float (&cf)[2][8],
+template <class Sch, int B, int S, bool TR, bool DIRECT, typename T, typename TB>
+__device__ __forceinline__ void round_compute(const RowParams& p, float* tile, int g, const float (&craw)[2][8],
                                               int64_t row0, int nr, int j) {
+  float cf[2][8];
+  decode_coef<B, TB, TR>(craw, cf);
   using Lay = typename Sch::Lay;
   constexpr int D = Sch::D;
   constexpr int NH = B > 4 ? 2 : 1;
@@ -252,11 +278,13 @@ __device__ __forceinline__ void read_inputs(const float* tile, int g, int j, flo
 // round's inputs are read after those writes (so the next round waits only
 // for its own reads and the writes before them, never for the last writes),
 // and the h = 1 outputs go last.  Radix 8 only (two output halves).
-template <class Sch, int B, int S, bool DIRECT, bool NEXT, typename T>
-__device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, int gn, const float (&cf)[2][8],
-                                               const float (&xv)[2][8], float (&xn)[2][8], int64_t row0, int nr,
-                                               int j) {
+template <class Sch, int B, int S, bool DIRECT, bool NEXT, typename T, typename TB, bool TR>
+__device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, int gn,
+                                               const float (&craw)[2][8], const float (&xv)[2][8],
+                                               float (&xn)[2][8], int64_t row0, int nr, int j) {
   static_assert(B == 8, "the pipelined round is written for radix 8");
+  float cf[2][8];
+  decode_coef<B, TB, TR>(craw, cf);
   using Lay = typename Sch::Lay;
   constexpr int PLANE = 4 * Lay::units(Sch::D);
   constexpr bool LIN = linear_stage<Lay, Sch::D, B, S>();
@@ -370,7 +398,7 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   load_coef<Sp::B, TB, TR>(rs, p.st[tp], grp_round<Sp::S>((rp + rot) % Rp), lane_grp<Sp::S>(gA, gB), j,
                            cf[(N + 3) % 4]);
   __builtin_amdgcn_sched_barrier(0);
-  products_write<Sch, B, S, DIRECT, (r + 1 < R), T>(p, tile, grp_round<S>((r + rot) % R) + gl,
+  products_write<Sch, B, S, DIRECT, (r + 1 < R), T, TB, TR>(p, tile, grp_round<S>((r + rot) % R) + gl,
                                                    grp_round<S>((r + 1 + rot) % R) + gl, cf[N % 4], xv[N % 2],
                                                    xv[(N + 1) % 2], row0, nr, j);
   __builtin_amdgcn_sched_barrier(0);
@@ -601,15 +629,15 @@ __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, con
   const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   // rounds 0..4: X holds round 0
   load_coef<8, TB, TR>(rs, sd, 1 * kGPR, gb, j, as8(Y));
-  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 0 * kGPR + gb, as8(X), 0, 0, j);
+  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 0 * kGPR + gb, as8(X), 0, 0, j);
   load_coef<8, TB, TR>(rs, sd, 2 * kGPR, gb, j, as8(X));
-  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 1 * kGPR + gb, as8(Y), 0, 0, j);
+  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 1 * kGPR + gb, as8(Y), 0, 0, j);
   load_coef<8, TB, TR>(rs, sd, 3 * kGPR, gb, j, as8(Y));
-  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 2 * kGPR + gb, as8(X), 0, 0, j);
+  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 2 * kGPR + gb, as8(X), 0, 0, j);
   load_coef<8, TB, TR>(rs, sd, 4 * kGPR, gb, j, as8(X));
-  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 3 * kGPR + gb, as8(Y), 0, 0, j);
+  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 3 * kGPR + gb, as8(Y), 0, 0, j);
   next(Y);   // the next stage's round 0 goes to Y
-  round_compute<Sch, 8, S, TR, false, uint16_t>(p, tile, 4 * kGPR + gb, as8(X), 0, 0, j);
+  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 4 * kGPR + gb, as8(X), 0, 0, j);
   __syncthreads();
 }
 

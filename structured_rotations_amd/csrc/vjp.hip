@@ -10,11 +10,15 @@
 //   dL/dx = D_s g_0.
 // The forward launches store x_1 .. x_{m-1} (fp32) in the workspace; x_0 is
 // re-read from x.  Each backward launch handles one stage: a thread owns one
-// group (half a group for radices 6..8) and a chunk of rows, keeps its part
-// of the group's block and of its b x b gradient in registers, and writes the
-// gradient of its chunk to a slot of its own;
-// a last launch sums the slots in a fixed order (no atomics, so the result
-// does not depend on scheduling).  Radices up to 8.
+// group (half a group for radices 6..8) and a chunk of rows, and keeps its
+// part of the group's block and of its b x b gradient in registers.  The
+// four waves of a workgroup own the same 64 groups over four consecutive
+// row chunks; they add their gradients through LDS in wave order and write
+// one slot per workgroup (at ~160 registers a thread, three such workgroups
+// fit on a CU).  A last launch sums the slots in slot order.  No atomics
+// anywhere, so the result does not depend on scheduling.  Radices up to 8.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -23,6 +27,8 @@ namespace harp {
 namespace {
 
 constexpr int kVjpThreads = 256;
+constexpr int kBwdWaves = 4;                    // row chunks per backward workgroup
+constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int64_t kVjpTargetThreads = 262144;   // threads per stage launch (group x row chunk)
 
 struct VjpStage {
@@ -50,8 +56,10 @@ struct VjpArgs {
   int64_t ldo;
   int o_bf16;
   int o_sign;
-  float* partial;            // backward: [nchunk][n_blk]
+  float* partial;            // backward: [nchunk / kBwdWaves][n_blk]
   int64_t n_blk;
+  int vec1;                  // backward: stride-1 stage whose rows of x_t, g_{t+1} and the output
+                             // allow 16-byte (8-byte for 4 bf16) accesses of a group's coordinates
 };
 
 template <typename TB>
@@ -132,99 +140,181 @@ __device__ __forceinline__ void st_t<uint16_t>(uint16_t* p, int64_t i, float v) 
   p[i] = (uint16_t)f32_to_bf16_rne(v);
 }
 
-// g_t = S_t^T g_{t+1} and the chunk's sum of g_{t+1}[c] x_t[c]^T.  TX, TG, TO:
-// element types of x_t, g_{t+1} and the output (bf16 only where they are the
-// caller's rows: x and dx for t = 0, dy for t = m - 1).
+// The b consecutive values of a group in a stride-1 stage, as 16-byte (or,
+// for 4 bf16, 8-byte) loads.
+template <int B, typename T>
+__device__ __forceinline__ void ld_vec(const T* p, float (&v)[B]) {
+  if constexpr (B != 4 && B != 8) {
+    (void)p;   // never reached: only radices 4 and 8 take the vector path
+    (void)v;
+  } else if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+    for (int q = 0; q < B / 4; ++q) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(p + 4 * q);
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+  } else if constexpr (B == 8) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  }
+}
+
+// 4 consecutive outputs (16 bytes of fp32 or 8 of bf16).
+template <typename T>
+__device__ __forceinline__ void st_vec4(T* p, const float (&o)[4]) {
+  if constexpr (std::is_same<T, float>::value)
+    *reinterpret_cast<f32x4*>(p) = f32x4{o[0], o[1], o[2], o[3]};
+  else
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2_hw(o[0], o[1]), pack_bf16x2_hw(o[2], o[3])};
+}
+
+template <int B>
+constexpr bool vec1_ok() {
+  return B == 8 || B == 4;
+}
+
+// g_t = S_t^T g_{t+1} and the sum over the rows of g_{t+1}[c] x_t[c]^T.  TX,
+// TG, TO: element types of x_t, g_{t+1} and the output (bf16 only where they
+// are the caller's rows: x and dx for t = 0, dy for t = m - 1).  Workgroup
+// (chunk block cb, group block gs): lane l of wave w owns the l-th
+// (group, half) pair of block gs over row chunk kBwdWaves * cb + w.
 template <int B, typename TB, typename TX, typename TG, typename TO>
-__global__ void __launch_bounds__(kVjpThreads) vjp_bwd_kernel(VjpArgs a) {
+__global__ void __launch_bounds__(kBwdThreads) vjp_bwd_kernel(VjpArgs a) {
   constexpr int H = bwd_split<B>();
   constexpr int RH = (B + H - 1) / H;            // rows (and columns) per thread
-  const int64_t id = (int64_t)blockIdx.x * kVjpThreads + threadIdx.x;
-  if (id >= (int64_t)a.st.ngroups * a.nchunk * H) return;
-  const int h = (int)(id % H);
-  const int64_t gid = id / H;
-  const int c = (int)(gid % a.st.ngroups);
-  const int chunk = (int)(gid / a.st.ngroups);
+  constexpr int NA = RH * B;                     // gradient entries per thread
+  __shared__ float red[kBwdWaves - 1][NA][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t npair = (int64_t)a.st.ngroups * H;
+  const int nsb = (int)((npair + 63) / 64);
+  const int gs = (int)(blockIdx.x % nsb);
+  const int cb = (int)(blockIdx.x / nsb);
+  const int64_t pid = (int64_t)gs * 64 + lane;
+  const bool valid = pid < npair;                // uniform per wave except in the last group block
+  const int h = (int)(pid % H);
+  const int c = valid ? (int)(pid / H) : 0;
+  const int chunk = cb * kBwdWaves + wave;
   const int s = a.st.s;
   const int64_t base = (int64_t)(c / s) * B * s + c % s;
-  // blk[r][kk] = B[r][h * RH + kk]: the block columns this thread's outputs need
-  float blk[B][RH];
-  {
-    const TB* bp = static_cast<const TB*>(a.blocks) + a.st.blk_off + (int64_t)c * B * B;
-    const float sc = sizeof(TB) == 1 ? a.scales[a.st.grp_off + c] : 1.0f;
-#pragma unroll
-    for (int r = 0; r < B; ++r)
-#pragma unroll
-      for (int kk = 0; kk < RH; ++kk) {
-        const int k = h * RH + kk;
-        blk[r][kk] = k < B ? coef_at<TB>(bp, r * B + k) * sc : 0.0f;
-      }
-  }
-  float xs[B], os[RH];
-#pragma unroll
-  for (int j = 0; j < B; ++j) xs[j] = a.x_sign ? (float)a.signs[base + j * s] : 1.0f;
-#pragma unroll
-  for (int kk = 0; kk < RH; ++kk) {
-    const int k = h * RH + kk;
-    os[kk] = (a.o_sign && k < B) ? (float)a.signs[base + k * s] : 1.0f;
-  }
   float acc[RH][B];
 #pragma unroll
   for (int rr = 0; rr < RH; ++rr)
 #pragma unroll
     for (int k = 0; k < B; ++k) acc[rr][k] = 0.0f;
-  const int64_t r0 = (int64_t)chunk * a.rpc;
-  const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
-  const TG* gin = static_cast<const TG*>(a.gin) + base;
-  const TX* xin = static_cast<const TX*>(a.xin) + base;
-  TO* out = static_cast<TO*>(a.out) + base;
-  for (int64_t row = r0; row < r1; ++row) {
-    const TG* gr = gin + row * a.ldg;
-    const TX* xr = xin + row * a.ldx;
-    float g[B], v[B];
+  if (valid) {
+    // blk[r][kk] = B[r][h * RH + kk]: the block columns this thread's outputs need
+    float blk[B][RH];
+    {
+      const TB* bp = static_cast<const TB*>(a.blocks) + a.st.blk_off + (int64_t)c * B * B;
+      const float sc = sizeof(TB) == 1 ? a.scales[a.st.grp_off + c] : 1.0f;
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      g[j] = ld_t<TG>(gr, j * s);
-      v[j] = ld_t<TX>(xr, j * s) * xs[j];
+      for (int r = 0; r < B; ++r)
+#pragma unroll
+        for (int kk = 0; kk < RH; ++kk) {
+          const int k = h * RH + kk;
+          blk[r][kk] = k < B ? coef_at<TB>(bp, r * B + k) * sc : 0.0f;
+        }
     }
+    float xs[B], os[RH];
 #pragma unroll
-    for (int rr = 0; rr < RH; ++rr) {
-      const int r = h * RH + rr;
-      const float gv = r < B ? g[r < B ? r : 0] : 0.0f;
+    for (int j = 0; j < B; ++j) xs[j] = a.x_sign ? (float)a.signs[base + j * s] : 1.0f;
 #pragma unroll
-      for (int k = 0; k < B; ++k) acc[rr][k] = fmaf(gv, v[k], acc[rr][k]);
+    for (int kk = 0; kk < RH; ++kk) {
+      const int k = h * RH + kk;
+      os[kk] = (a.o_sign && k < B) ? (float)a.signs[base + k * s] : 1.0f;
     }
-    if (a.out != nullptr) {
-      TO* orow = out + row * a.ldo;
+    const int64_t r0 = (int64_t)chunk * a.rpc;
+    const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
+    const TG* gin = static_cast<const TG*>(a.gin) + base;
+    const TX* xin = static_cast<const TX*>(a.xin) + base;
+    TO* out = static_cast<TO*>(a.out) + base;
+    const bool v1 = vec1_ok<B>() && a.vec1;
+    for (int64_t row = r0; row < r1; ++row) {
+      const TG* gr = gin + row * a.ldg;
+      const TX* xr = xin + row * a.ldx;
+      float g[B], v[B];
+      if (v1) {
+        ld_vec<B, TG>(gr, g);
+        ld_vec<B, TX>(xr, v);
 #pragma unroll
-      for (int kk = 0; kk < RH; ++kk) {
-        const int k = h * RH + kk;
-        if (k < B) {
+        for (int j = 0; j < B; ++j) v[j] *= xs[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+          g[j] = ld_t<TG>(gr, j * s);
+          v[j] = ld_t<TX>(xr, j * s) * xs[j];
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RH; ++rr) {
+        const int r = h * RH + rr;
+        const float gv = r < B ? g[r < B ? r : 0] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < B; ++k) acc[rr][k] = fmaf(gv, v[k], acc[rr][k]);
+      }
+      if (a.out != nullptr) {
+        TO* orow = out + row * a.ldo;
+        float o4[RH];
+#pragma unroll
+        for (int kk = 0; kk < RH; ++kk) {
+          const int k = h * RH + kk;
           float o = 0.0f;
 #pragma unroll
           for (int r = 0; r < B; ++r) o = fmaf(blk[r][kk], g[r], o);
-          st_t<TO>(orow, k * s, o * os[kk]);
+          o4[kk] = k < B ? o * os[kk] : 0.0f;
+        }
+        if constexpr (RH == 4) {
+          if (v1) {
+            st_vec4<TO>(orow + h * RH, o4);
+            continue;
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < RH; ++kk) {
+          const int k = h * RH + kk;
+          if (k < B) st_t<TO>(orow, k * s, o4[kk]);
         }
       }
     }
   }
-  float* pp = a.partial + (int64_t)chunk * a.n_blk + a.st.blk_off + (int64_t)c * B * B;
+  // fixed-order sum over the workgroup's row chunks: wave 0 adds waves 1, 2, ... in order
+  if (wave > 0) {
 #pragma unroll
-  for (int rr = 0; rr < RH; ++rr) {
-    const int r = h * RH + rr;
-    if (r < B) {
+    for (int rr = 0; rr < RH; ++rr)
 #pragma unroll
-      for (int k = 0; k < B; ++k) pp[r * B + k] = acc[rr][k];
+      for (int k = 0; k < B; ++k) red[wave - 1][rr * B + k][lane] = acc[rr][k];
+  }
+  __syncthreads();
+  if (wave == 0 && valid) {
+#pragma unroll
+    for (int w = 0; w < kBwdWaves - 1; ++w)
+#pragma unroll
+      for (int rr = 0; rr < RH; ++rr)
+#pragma unroll
+        for (int k = 0; k < B; ++k) acc[rr][k] += red[w][rr * B + k][lane];
+    float* pp = a.partial + (int64_t)cb * a.n_blk + a.st.blk_off + (int64_t)c * B * B;
+#pragma unroll
+    for (int rr = 0; rr < RH; ++rr) {
+      const int r = h * RH + rr;
+      if (r < B) {
+#pragma unroll
+        for (int k = 0; k < B; ++k) pp[r * B + k] = acc[rr][k];
+      }
     }
   }
 }
 
-__global__ void __launch_bounds__(kVjpThreads) vjp_reduce_kernel(const float* partial, int nchunk, int64_t n_blk,
+__global__ void __launch_bounds__(kVjpThreads) vjp_reduce_kernel(const float* partial, int nslot, int64_t n_blk,
                                                                  float* dblocks) {
   const int64_t i = (int64_t)blockIdx.x * kVjpThreads + threadIdx.x;
   if (i >= n_blk) return;
   float acc = 0.0f;
-  for (int ch = 0; ch < nchunk; ++ch) acc += partial[(int64_t)ch * n_blk + i];
+  for (int sl = 0; sl < nslot; ++sl) acc += partial[(int64_t)sl * n_blk + i];
   dblocks[i] = acc;
 }
 
@@ -235,13 +325,16 @@ int vjp_chunks(const Plan& pl, int64_t rows) {
   int64_t n = (kVjpTargetThreads + ng - 1) / ng;
   if (n > rows) n = rows;
   if (n < 1) n = 1;
-  return (int)n;
+  // whole backward workgroups (chunks past the last row are empty)
+  return (int)((n + kBwdWaves - 1) / kBwdWaves * kBwdWaves);
 }
 
 template <int B, typename TB>
 hipError_t launch_stage(bool fwd, const VjpArgs& a, hipStream_t st) {
-  const int64_t n = (int64_t)a.st.ngroups * a.nchunk * (fwd ? 1 : bwd_split<B>());
-  const int64_t grid = (n + kVjpThreads - 1) / kVjpThreads;
+  const int64_t n = (int64_t)a.st.ngroups * a.nchunk;
+  const int64_t grid = fwd ? (n + kVjpThreads - 1) / kVjpThreads
+                           : ((int64_t)a.st.ngroups * bwd_split<B>() + 63) / 64 * (a.nchunk / kBwdWaves);
+  const dim3 blk(fwd ? kVjpThreads : kBwdThreads);
   if (fwd) {
     if (a.x_bf16)
       hipLaunchKernelGGL((vjp_fwd_kernel<B, TB, uint16_t>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a);
@@ -252,12 +345,12 @@ hipError_t launch_stage(bool fwd, const VjpArgs& a, hipStream_t st) {
     using H16 = uint16_t;
     const int code = (a.x_bf16 ? 4 : 0) | (a.g_bf16 ? 2 : 0) | (a.o_bf16 ? 1 : 0);
     switch (code) {
-      case 0: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, F, F, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
-      case 5: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, F, H16>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, F, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, F, H16, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
-      case 7: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, H16, H16>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
-      case 6: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, H16, F>), dim3((unsigned)grid), dim3(kVjpThreads), 0, st, a); break;
+      case 0: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, F, F, F>), dim3((unsigned)grid), blk, 0, st, a); break;
+      case 5: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, F, H16>), dim3((unsigned)grid), blk, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, F, F>), dim3((unsigned)grid), blk, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, F, H16, F>), dim3((unsigned)grid), blk, 0, st, a); break;
+      case 7: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, H16, H16>), dim3((unsigned)grid), blk, 0, st, a); break;
+      case 6: hipLaunchKernelGGL((vjp_bwd_kernel<B, TB, H16, H16, F>), dim3((unsigned)grid), blk, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -293,7 +386,7 @@ int64_t vjp_workspace_bytes(const Plan& pl, int64_t rows) {
   if (rows > (INT64_MAX / 256) / pl.d) return -1;
   const int64_t acts = (int64_t)(pl.m - 1) * rows * pl.d;
   const int64_t gbuf = (pl.m > 1 ? 2 : 0) * rows * pl.d;
-  const int64_t part = (int64_t)vjp_chunks(pl, rows) * pl.n_blk;
+  const int64_t part = (int64_t)(vjp_chunks(pl, rows) / kBwdWaves) * pl.n_blk;
   return 4 * (acts + gbuf + part);
 }
 
@@ -361,12 +454,24 @@ hipError_t launch_apply_vjp(const Plan& pl, const void* blocks, DT bdt, const fl
       a.out = gbuf + (int64_t)(k & 1) * rd;
       a.ldo = pl.d;
     }
+    if (a.st.s == 1) {
+      // stride 1: a group's coordinates are contiguous; vector accesses need
+      // every row of the three arrays to start on their alignment
+      const int xb = a.x_bf16 ? 2 : 4, gb = a.g_bf16 ? 2 : 4, ob = a.o_bf16 ? 2 : 4;
+      auto al = [](const void* ptr, int64_t ld, int eb, int bytes) {
+        return reinterpret_cast<uintptr_t>(ptr) % 16 == 0 && (ld * eb) % bytes == 0;
+      };
+      const int gbytes = a.st.b * 4;   // a group's fp32 bytes: 32 or 16
+      a.vec1 = al(a.xin, a.ldx, xb, a.st.b * xb < 16 ? a.st.b * xb : 16) &&
+               al(a.gin, a.ldg, gb, a.st.b * gb < 16 ? a.st.b * gb : 16) &&
+               al(a.out, a.ldo, ob, 4 * ob) && gbytes >= 16;
+    }
     hipError_t e = launch_stage_any(false, bdt, a, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t grid = (pl.n_blk + kVjpThreads - 1) / kVjpThreads;
-  hipLaunchKernelGGL(vjp_reduce_kernel, dim3((unsigned)grid), dim3(kVjpThreads), 0, stream, part, nchunk, pl.n_blk,
-                     dblocks);
+  hipLaunchKernelGGL(vjp_reduce_kernel, dim3((unsigned)grid), dim3(kVjpThreads), 0, stream, part, nchunk / kBwdWaves,
+                     pl.n_blk, dblocks);
   return hipGetLastError();
 }
 

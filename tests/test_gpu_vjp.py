@@ -144,3 +144,41 @@ def test_vjp_without_signs_and_one_row():
     rdx, rdb = O.apply_vjp(w["x"].astype(np.float64), sch, blocks_o, None, dy.astype(np.float64))
     assert_rows_close(from_dev(dx), rdx, TOL["f32"], "dx")
     assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, "dB")
+
+
+@pytest.mark.parametrize("sch,d", [((8, 8, 8, 8), 4096), ((4, 8, 4), 128)])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("pad", [0, 1, 8])
+def test_vjp_strided_rows(sch, d, io, pad):
+    """Row strides that keep or break the 16-byte alignment of the stride-1
+    stage's contiguous group accesses (dx and dB both checked); rows span
+    more than one row chunk per workgroup."""
+    print(f"\n[case] vjp strided {sch} io={io} pad={pad}", flush=True)
+    g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 300 + d + pad)
+    theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
+    gauss = I.gauss_mats(g_gauss, sch)
+    signs = I.rademacher(g_sign, d)
+    rows = 300
+    x = g_data.standard_normal((rows, d)).astype(np.float32)
+    dy = _dy(rows, d, io, 9)
+    if io == "bf16":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+
+    def wide(a):
+        t = torch.zeros((rows, d + pad), dtype=tdt, device="cuda")
+        t[:, :d] = torch.from_numpy(a).to(tdt).cuda()
+        return t[:, :d]
+
+    xd, dyd = wide(x), wide(dy)
+    dx = torch.full((rows, d + pad), 7.0, dtype=tdt, device="cuda")[:, :d]
+    blocks_g, _ = gpu_blocks(api, sch, d, theta, gauss, "f32")
+    _, db = api.harp_apply_vjp(sch, d, blocks_g, None, signs_dev(signs), xd, dyd, dx=dx)
+    torch.cuda.synchronize()
+    blocks_o = oracle_blocks(sch, d, theta, gauss, "f32")
+    rdx, rdb = O.apply_vjp(x.astype(np.float64), sch, blocks_o, signs.astype(float), dy.astype(np.float64))
+    assert_rows_close(dx.float().cpu().numpy(), rdx, TOL[io], f"{sch}/{io}/pad{pad} dx")
+    assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, f"{sch}/{io}/pad{pad} dB")
+    if pad:
+        base = dx.as_strided((rows, pad), (d + pad, 1), d)   # the pad columns beside each row
+        assert bool((base.float() == 7.0).all()), "dx written outside its rows"
