@@ -374,8 +374,8 @@ harp_status harp_rotate_weight(const harp_schedule* su, const void* blocks_u, co
     cut[++npass] = e;
     t = e;
   }
-  // Buffer chain: V pass reads w; every later pass reads what the previous
-  // one wrote; the final pass writes w_out.
+  // Buffer chain: the first pass reads w; every later pass reads what the
+  // previous one wrote; the final pass writes w_out.
   float* ws = static_cast<float*>(workspace);
   const void* src = w;
   int64_t lds_ = ldw;
@@ -389,19 +389,25 @@ harp_status harp_rotate_weight(const harp_schedule* su, const void* blocks_u, co
     if (step == total - 1) { *ldd = ldo; *ddt = io; return w_out; }
     *ldd = ldm; *ddt = mdt; return mid;
   };
-  // V on the rows.
-  {
+  // U mixes the rows of W (it acts on every column) and V its columns (it
+  // acts on every row), so the passes commute.  In place, V goes first.  With an fp32
+  // workspace, the first and last passes convert between io_dtype and fp32
+  // and the middle ones run fp32 to fp32: a column pass opens and closes the
+  // chain (their 16-byte paths take either conversion) and V, whose fastest
+  // kernels keep one element type, runs fp32 to fp32 in between.
+  auto row_pass = [&]() -> harp_status {
     int64_t ldd; DT ddt;
     void* dst = dst_for(done, &ldd, &ddt);
     hipError_t e = harp::launch_apply_rows(pv, inv, blocks_v, bdt, scales_v, signs_v, src, lds_, sdt, dst, ldd,
                                            ddt, d_out, stream);
     if (e != hipSuccess) return launch_status(e, "harp_rotate_weight (row pass)");
     src = dst; lds_ = ldd; sdt = ddt; ++done;
-  }
+    return HARP_OK;
+  };
   // U on the columns: forward runs the passes in order with the sign read
   // with the first pass; the inverse runs them in reverse with the sign
   // written by the last pass.
-  for (int i = 0; i < npass; ++i) {
+  auto col_pass = [&](int i) -> harp_status {
     const int pi = inv ? npass - 1 - i : i;
     const int t0 = cut[pi], t1 = cut[pi + 1];
     int sign_mode = 0;
@@ -413,8 +419,19 @@ harp_status harp_rotate_weight(const harp_schedule* su, const void* blocks_u, co
                                            lds_, sdt, dst, ldd, ddt, d_in, stream);
     if (e != hipSuccess) return launch_status(e, "harp_rotate_weight (column pass)");
     src = dst; lds_ = ldd; sdt = ddt; ++done;
+    return HARP_OK;
+  };
+  const bool v_middle = ws != nullptr && npass >= 2;
+  harp_status st = HARP_OK;
+  if (v_middle) {
+    st = col_pass(0);
+    if (st == HARP_OK) st = row_pass();
+    for (int i = 1; i < npass && st == HARP_OK; ++i) st = col_pass(i);
+  } else {
+    st = row_pass();
+    for (int i = 0; i < npass && st == HARP_OK; ++i) st = col_pass(i);
   }
-  return HARP_OK;
+  return st;
 }
 
 harp_status rht_compose(const harp_schedule* s, int64_t d, const int8_t* signs, int32_t k, const void* x,

@@ -40,7 +40,9 @@ struct ColParams {
   int64_t ntiles;    // (d / nsub) * npanels
   int64_t ncols;
   int vec;           // 16-byte row segments and whole panels: aligned bases, ld and widths
-  int dup;           // chunk slots wrap around (some chunks have two owners)
+  int split_swap;    // store every finished chunk before any incoming one is written: chunk
+                     // slots wrap around (some chunks have two owners), or an output chunk is
+                     // made of two input chunks of different threads (fp32 in, bf16 out)
   uint32_t mag_ncb;  // ceil(2^32 / (pw / 64)) (0 for one block)
   uint32_t mag_cpr;  // same for the input chunks per tile row, pw / (16 / input element bytes)
   uint32_t mag_tot;  // same for the input chunks per tile, nsub * pw / (16 / input element bytes)
@@ -301,7 +303,7 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* v, float*) {
 // slot 0's finished data again), so every thread issues exactly MAXC loads
 // and stores per tile and the waits before a prefetched tile goes into LDS
 // count them exactly.  With fewer than 512 chunks a thread may have no chunk
-// of its own: then the slot wraps to another thread's chunk (p.dup).
+// of its own: then the slot wraps to another thread's chunk (p.split_swap).
 __device__ __forceinline__ int chunk_of(int j, int total, uint32_t mag_tot) {
   const int i = (int)threadIdx.x + j * 512;
   return i < total ? i : (total >= 512 ? (int)threadIdx.x : i - udiv(i, mag_tot) * total);
@@ -378,6 +380,8 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
         // fp32 in, bf16 out: pairs of input chunks make one output chunk;
         // the even chunk of a pair stores both halves
         static_assert(VO == 2 * VI, "chunk widths");
+        // (both chunks of a pair lie in one tile row, so the slot's sign bit
+        // is the pair's)
         if ((ch & 1) == 0) {
           float v[VO];
 #pragma unroll
@@ -385,8 +389,9 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
             const f32x4 q4 = *reinterpret_cast<const f32x4*>(loc + e);
             v[e] = q4.x; v[e + 1] = q4.y; v[e + 2] = q4.z; v[e + 3] = q4.w;
           }
-          st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI,
-                    pack_chunk(v, static_cast<TOUT*>(nullptr)));
+          u32x4 o = pack_chunk(v, static_cast<TOUT*>(nullptr));
+          if (p.sign_mode == 2 && ((smask >> j) & 1u)) o = flip_chunk(o, ChunkSign<TOUT>::m);
+          st_stream(y + (done.row_base + (int64_t)u * p.suf) * p.ldy + done.col0 + ch * VI, o);
         }
       }
     }
@@ -408,15 +413,16 @@ __device__ __forceinline__ void col_swap_part(const ColParams& p, const ColTile&
 // smask holds, per slot, whether the row of the tile in LDS has a negative
 // sign: it is the same row in every tile of the pass, and the swap replaces
 // it with the incoming tile's.
-// When slots wrap around to other threads' chunks (p.dup), a chunk has two
-// owners, and one of them could overwrite it before the other has stored it:
-// then every store is done first and a barrier separates them from the
-// writes.
+// When slots wrap around to other threads' chunks, a chunk has two owners,
+// and one of them could overwrite it before the other has stored it; with
+// fp32 in and bf16 out, the thread of an even chunk stores its odd neighbour
+// too, which another thread replaces.  In both cases (p.split_swap) every
+// store is done first and a barrier separates them from the writes.
 template <typename TIN, typename TOUT, int MAXC>
 __device__ __forceinline__ void col_swap(const ColParams& p, const ColTile& done, bool has_done, bool has_next,
                                          const u32x4 (&r)[MAXC], const uint8_t (&sg)[MAXC], uint32_t& smask,
                                          float* tile) {
-  if (p.dup) {
+  if (p.split_swap) {
     if (has_done) col_swap_part<TIN, TOUT, MAXC>(p, done, true, false, r, sg, smask, tile);
     __syncthreads();
     if (has_next) col_swap_part<TIN, TOUT, MAXC>(p, done, false, true, r, sg, smask, tile);
@@ -540,21 +546,13 @@ template <typename TIN> struct ColMaxc;
 template <> struct ColMaxc<uint16_t> { static constexpr int lo = 4, hi = 8; };
 template <> struct ColMaxc<float> { static constexpr int lo = 8, hi = 16; };
 
-// fp32 in, bf16 out never takes the 16-byte path (see the launch), so it has
-// no 16-byte kernels.
-template <typename TIN, typename TOUT>
-constexpr bool col_vec_io() { return !(std::is_same<TIN, float>::value && std::is_same<TOUT, uint16_t>::value); }
 
 template <typename TIN, typename TOUT, typename TB, bool BIG>
 hipError_t launch_cols_k(const ColParams& p, int maxc, int grid, size_t lds, hipStream_t st) {
   void (*kern)(ColParams) = col_pass_kernel<TIN, TOUT, TB, BIG, false, 1>;
-  if constexpr (col_vec_io<TIN, TOUT>()) {
-    if (p.vec)
-      kern = maxc <= ColMaxc<TIN>::lo ? col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::lo>
-                                      : col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::hi>;
-  } else {
-    if (p.vec) return hipErrorInvalidValue;
-  }
+  if (p.vec)
+    kern = maxc <= ColMaxc<TIN>::lo ? col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::lo>
+                                    : col_pass_kernel<TIN, TOUT, TB, BIG, true, ColMaxc<TIN>::hi>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -672,8 +670,8 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   const int maxc = (int)(((int64_t)nsub * (pw / vi) + 511) / 512);
   const int maxc_cap = in_dt == DT::F32 ? 16 : 8;
   p.vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && (ldx * ib) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0 &&
-          (ldy * ob) % 16 == 0 && ncols % pw == 0 && maxc <= maxc_cap && !(in_dt == DT::F32 && out_dt == DT::BF16);
-  p.dup = (int64_t)nsub * (pw / vi) < 512;
+          (ldy * ob) % 16 == 0 && ncols % pw == 0 && maxc <= maxc_cap;
+  p.split_swap = (int64_t)nsub * (pw / vi) < 512 || (in_dt == DT::F32 && out_dt == DT::BF16);
   const size_t lds = ((size_t)nsub * pw + (size_t)2 * p.cslot) * sizeof(float);
   int64_t grid = (int64_t)cus_for_cols() * (lds > 80 * 1024 ? 1 : 2);
   if (grid > p.ntiles) grid = p.ntiles;

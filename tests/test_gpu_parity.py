@@ -13,6 +13,7 @@ import torch
 
 from oracle import harp_oracle as O
 from structured_rotations_amd import api
+from structured_rotations_amd import inputs as I
 from structured_rotations_amd import workloads as W
 from tests.parity_util import (TOL, TOL_BF16_THREE_ROUNDINGS, assert_rows_close, from_dev, gpu_blocks, oracle_blocks,
                                signs_dev, to_dev)
@@ -386,6 +387,28 @@ def test_rotate_weight_block_types(blk, io):
     c["sv_s"] = np.where(rng.integers(0, 2, dv) == 1, 1, -1).astype(np.int8)
     c["w"] = W.round_io((rng.standard_normal((du, dv)) * 0.02).astype(np.float32), io)
     _rotate_round_trip(c, io, blk, None, f"two-sided {blk}/{io}")
+
+
+@pytest.mark.parametrize("su,du", [((8, 8, 8), 512), ((8, 8, 8, 2), 1024), ((8, 8, 8, 3, 3), 4608)])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_workspace_whole_panels(su, du, io):
+    # fp32 workspace, whole panels (the 16-byte path of the column passes):
+    # one U pass (V first, then U from fp32 back to io_dtype), or two (a
+    # column pass from io_dtype to fp32, V fp32 to fp32, a column pass from
+    # fp32 back to io_dtype); the inverse writes the U signs in its last pass
+    print(f"\n[case] two-sided workspace su={su} io={io}", flush=True)
+    rng = np.random.default_rng(43 + du)
+    sv, dv = (8, 16), 128
+    c = {"su": su, "sv": sv, "du": du, "dv": dv}
+    c["tu"] = rng.standard_normal(sum(O.theta_counts(su, du))) * 0.05
+    c["tv"] = rng.standard_normal(sum(O.theta_counts(sv, dv))) * 0.05
+    c["gu"] = I.gauss_mats(rng, su)
+    c["gv"] = np.zeros(0)
+    c["su_s"] = np.where(rng.integers(0, 2, du) == 1, 1, -1).astype(np.int8)
+    c["sv_s"] = np.where(rng.integers(0, 2, dv) == 1, 1, -1).astype(np.int8)
+    c["w"] = W.round_io((rng.standard_normal((du, dv)) * 0.02).astype(np.float32), io)
+    ws = torch.empty(api.harp_rotate_weight_workspace(du, dv) // 4, dtype=torch.float32, device="cuda")
+    _rotate_round_trip(c, io, "f32", ws, f"two-sided workspace {su}/{io}")
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
