@@ -94,21 +94,47 @@ constexpr int rounds_before_rt(int t) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coef_rsrc(const RowParams& p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.blocks), (short)0, -1, 0x00020000);
 }
+// Per-group fp32 scales of int8 blocks (a valid address, never read, otherwise).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const RowParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.scales ? p.scales : static_cast<const float*>(p.blocks)),
+                                           (short)0, -1, 0x00020000);
+}
 
 // cf[h][k] = C[4h + j][k] of group g0 + gb (C = B forward, B^T inverse; g0
 // uniform); lanes whose row 4h + j is past the radix re-read row B - 1 (their
-// outputs are dropped).  Rows of bf16 blocks (forward) stay packed, two per
-// word, as they arrive: decode_coef widens them where the round uses them,
-// so no wait for the load lands where it is issued (bf16 blocks then move
-// half the bytes of fp32 at no extra stall).  The inverse reads columns one
-// element at a time and widens each at once (deferring those measured
-// slower).
+// outputs are dropped).  Rows of bf16 and int8 blocks (forward) stay packed
+// as they arrive, the int8 group scale beside them: decode_coef widens them
+// where the round uses them, so no wait for the load lands where it is
+// issued (bf16 blocks then move half the bytes of fp32 at no extra stall).
+// The inverse reads columns one element at a time and widens each at once
+// (deferring those measured slower).
 template <int B, typename TB, bool TR>
-__device__ __forceinline__ void load_coef(__amdgpu_buffer_rsrc_t rs, const StageFast& sd, int g0, int gb, int j,
+__device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g0, int gb, int j,
                                           float (&cf)[2][8]) {
   constexpr int NH = B > 4 ? 2 : 1;
   constexpr int SZ = (int)sizeof(TB);
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   const int soff = __builtin_amdgcn_readfirstlane((sd.blk_off + g0 * B * B) * SZ);
+  if constexpr (std::is_same<TB, int8_t>::value) {
+    static_assert(B == 8, "int8 rounds are radix 8");
+    const float sc = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(scale_rsrc(p), (sd.grp_off + g0 + gb) * 4, 0, 0));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = 4 * h + j;
+      if constexpr (!TR) {
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, gb * 64 + o * 8, soff, 0);
+        cf[h][0] = __uint_as_float(a.x);
+        cf[h][1] = __uint_as_float(a.y);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          cf[h][k] = (float)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, gb * 64 + o + k * 8, soff, 0) * sc;
+      }
+    }
+    if constexpr (!TR) cf[0][2] = sc;   // an unused slot of the forward layout
+    return;
+  }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int o = 4 * h + j < B ? 4 * h + j : B - 1;
@@ -152,7 +178,16 @@ __device__ __forceinline__ void decode_coef(const float (&raw)[2][8], float (&cf
   constexpr int NH = B > 4 ? 2 : 1;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    if constexpr (!std::is_same<TB, float>::value && !TR && (B == 8 || B == 4)) {
+    if constexpr (std::is_same<TB, int8_t>::value && !TR) {
+      // code c as the byte c + 128, then (c + 128) sc - 128 sc: c * sc rounded once
+      const float sc = raw[0][2], off = -128.0f * sc;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t u = __float_as_uint(raw[h][w]) ^ 0x80808080u;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) cf[h][4 * w + n] = fmaf((float)((u >> (8 * n)) & 0xffu), sc, off);
+      }
+    } else if constexpr (std::is_same<TB, uint16_t>::value && !TR && (B == 8 || B == 4)) {
 #pragma unroll
       for (int i = 0; i < B / 2; ++i) {
         cf[h][2 * i] = bf16_lo(__float_as_uint(raw[h][i]));
@@ -392,10 +427,9 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   constexpr int rp = NP - rounds_before_rt<Sch>(tp);
   using Sp = typename At<tp, typename Sch::L>::type;
   constexpr int Rp = Sch::D / Sp::B / kGPR;
-  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   const int gl = lane_grp<S>(gA, gB);
   __builtin_amdgcn_sched_barrier(0);
-  load_coef<Sp::B, TB, TR>(rs, p.st[tp], grp_round<Sp::S>((rp + rot) % Rp), lane_grp<Sp::S>(gA, gB), j,
+  load_coef<Sp::B, TB, TR>(p, p.st[tp], grp_round<Sp::S>((rp + rot) % Rp), lane_grp<Sp::S>(gA, gB), j,
                            cf[(N + 3) % 4]);
   __builtin_amdgcn_sched_barrier(0);
   products_write<Sch, B, S, DIRECT, (r + 1 < R), T, TB, TR>(p, tile, grp_round<S>((r + rot) % R) + gl,
@@ -455,7 +489,7 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
 #pragma unroll
   for (int n = 0; n < 3; ++n) {
     // rounds 0..2 all lie in stage 0 (it has at least 4 rounds)
-    load_coef<S0::B, TB, TR>(coef_rsrc(p), p.st[0], grp_round<S0::S>((n + rot) % R0), lane_grp<S0::S>(gA, gB), j,
+    load_coef<S0::B, TB, TR>(p, p.st[0], grp_round<S0::S>((n + rot) % R0), lane_grp<S0::S>(gA, gB), j,
                              cf[n]);
   }
   __syncthreads();
@@ -490,23 +524,37 @@ __device__ __forceinline__ const float (&as8(const Cbuf& c))[2][8] {
   return *reinterpret_cast<const float(*)[2][8]>(&c.v[0]);
 }
 
+// sc: the group's scale (int8 blocks only)
 template <typename TB>
-__device__ __forceinline__ float ld_coef1(__amdgpu_buffer_rsrc_t rs, int voff_el, int soff_bytes) {
+__device__ __forceinline__ float ld_coef1(__amdgpu_buffer_rsrc_t rs, int voff_el, int soff_bytes, float sc) {
   if constexpr (std::is_same<TB, float>::value)
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff_el * 4, soff_bytes, 0));
-  else
+  else if constexpr (std::is_same<TB, uint16_t>::value)
     return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff_el * 2, soff_bytes, 0) << 16);
+  else
+    return (float)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, voff_el, soff_bytes, 0) * sc;
 }
 // four consecutive coefficients starting at a 4-aligned element
 template <typename TB>
-__device__ __forceinline__ void ld_coef4(__amdgpu_buffer_rsrc_t rs, int voff_el, int soff_bytes, float* d) {
+__device__ __forceinline__ void ld_coef4(__amdgpu_buffer_rsrc_t rs, int voff_el, int soff_bytes, float sc, float* d) {
   if constexpr (std::is_same<TB, float>::value) {
     const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_el * 4, soff_bytes, 0);
     d[0] = __uint_as_float(a.x); d[1] = __uint_as_float(a.y); d[2] = __uint_as_float(a.z); d[3] = __uint_as_float(a.w);
-  } else {
+  } else if constexpr (std::is_same<TB, uint16_t>::value) {
     const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_el * 2, soff_bytes, 0);
     d[0] = bf16_lo(a.x); d[1] = bf16_hi(a.x); d[2] = bf16_lo(a.y); d[3] = bf16_hi(a.y);
+  } else {
+    const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(rs, voff_el, soff_bytes, 0);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) d[n] = (float)(int8_t)(a >> (8 * n)) * sc;
   }
+}
+template <typename TB>
+__device__ __forceinline__ float ld_scale(const RowParams& p, int grp) {
+  if constexpr (std::is_same<TB, int8_t>::value)
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scale_rsrc(p), grp * 4, 0, 0));
+  else
+    return 1.0f;
 }
 
 // Tail coefficients for chunk g = g0 + gb (g0 uniform).  s5: the radix-5
@@ -514,9 +562,10 @@ __device__ __forceinline__ void ld_coef4(__amdgpu_buffer_rsrc_t rs, int voff_el,
 // o = min(4h + j, 4), and the two 2 x 2 blocks of columns o (h = 0, 1).
 // Inverse: c5[d4][h][k] = C5_{2g+d4}[k][o] and all five 2 x 2 blocks.
 template <typename TB, bool TR>
-__device__ __forceinline__ void load_tail(__amdgpu_buffer_rsrc_t rs, const StageFast& s5, const StageFast& s2, int g0,
+__device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s5, const StageFast& s2, int g0,
                                           int gb, int j, Cbuf& c) {
   constexpr int SZ = (int)sizeof(TB);
+  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   const int soff5 = __builtin_amdgcn_readfirstlane((s5.blk_off + g0 * 2 * 25) * SZ);
   const int soff2 = __builtin_amdgcn_readfirstlane((s2.blk_off + g0 * 5 * 4) * SZ);
 #pragma unroll
@@ -525,27 +574,29 @@ __device__ __forceinline__ void load_tail(__amdgpu_buffer_rsrc_t rs, const Stage
     for (int h = 0; h < 2; ++h) {
       const int o = 4 * h + j < 5 ? 4 * h + j : 4;
       const int base = (2 * gb + d4) * 25;
+      const float sc = ld_scale<TB>(p, s5.grp_off + 2 * (g0 + gb) + d4);
       float* d = &c.v[(d4 * 2 + h) * 5];
       if constexpr (!TR && std::is_same<TB, float>::value) {
         // row o of the block: 5 consecutive floats, 4-byte aligned (a
         // 16-byte load needs only dword alignment here)
         const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + o * 5) * 4, soff5, 0);
         d[0] = __uint_as_float(a.x); d[1] = __uint_as_float(a.y); d[2] = __uint_as_float(a.z); d[3] = __uint_as_float(a.w);
-        d[4] = ld_coef1<TB>(rs, base + o * 5 + 4, soff5);
+        d[4] = ld_coef1<TB>(rs, base + o * 5 + 4, soff5, sc);
       } else {
 #pragma unroll
-        for (int k = 0; k < 5; ++k) d[k] = ld_coef1<TB>(rs, base + (TR ? k * 5 + o : o * 5 + k), soff5);
+        for (int k = 0; k < 5; ++k) d[k] = ld_coef1<TB>(rs, base + (TR ? k * 5 + o : o * 5 + k), soff5, sc);
       }
     }
   if constexpr (!TR) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int o = 4 * h + j < 5 ? 4 * h + j : 4;
-      ld_coef4<TB>(rs, (5 * gb + o) * 4, soff2, &c.v[20 + 4 * h]);
+      ld_coef4<TB>(rs, (5 * gb + o) * 4, soff2, ld_scale<TB>(p, s2.grp_off + 5 * (g0 + gb) + o), &c.v[20 + 4 * h]);
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 5; ++k) ld_coef4<TB>(rs, (5 * gb + k) * 4, soff2, &c.v[20 + 4 * k]);
+    for (int k = 0; k < 5; ++k)
+      ld_coef4<TB>(rs, (5 * gb + k) * 4, soff2, ld_scale<TB>(p, s2.grp_off + 5 * (g0 + gb) + k), &c.v[20 + 4 * k]);
   }
 }
 
@@ -626,15 +677,14 @@ template <class Lay, int S, bool TR, typename TB, typename NextLoad>
 __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, const StageFast& sd, Cbuf& X, Cbuf& Y,
                                             int gb, int j, NextLoad next) {
   using Sch = Sched<5120, Lay, List<St<8, S>>>;
-  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   // rounds 0..4: X holds round 0
-  load_coef<8, TB, TR>(rs, sd, 1 * kGPR, gb, j, as8(Y));
+  load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
   round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 0 * kGPR + gb, as8(X), 0, 0, j);
-  load_coef<8, TB, TR>(rs, sd, 2 * kGPR, gb, j, as8(X));
+  load_coef<8, TB, TR>(p, sd, 2 * kGPR, gb, j, as8(X));
   round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 1 * kGPR + gb, as8(Y), 0, 0, j);
-  load_coef<8, TB, TR>(rs, sd, 3 * kGPR, gb, j, as8(Y));
+  load_coef<8, TB, TR>(p, sd, 3 * kGPR, gb, j, as8(Y));
   round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 2 * kGPR + gb, as8(X), 0, 0, j);
-  load_coef<8, TB, TR>(rs, sd, 4 * kGPR, gb, j, as8(X));
+  load_coef<8, TB, TR>(p, sd, 4 * kGPR, gb, j, as8(X));
   round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 3 * kGPR + gb, as8(Y), 0, 0, j);
   next(Y);   // the next stage's round 0 goes to Y
   round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 4 * kGPR + gb, as8(X), 0, 0, j);
@@ -645,13 +695,12 @@ template <class Lay, bool TR, typename TB, typename NextLoad>
 __device__ __forceinline__ void stage_tail_5120(const RowParams& p, float* tile, const StageFast& s5,
                                                 const StageFast& s2, Cbuf& X, Cbuf& Y, int gb, int j,
                                                 NextLoad next) {
-  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   // rounds 0..3: X holds round 0
-  load_tail<TB, TR>(rs, s5, s2, 1 * kGPR, gb, j, Y);
+  load_tail<TB, TR>(p, s5, s2, 1 * kGPR, gb, j, Y);
   tail_round<Lay, TR>(tile, 0 * kGPR + gb, X, j);
-  load_tail<TB, TR>(rs, s5, s2, 2 * kGPR, gb, j, X);
+  load_tail<TB, TR>(p, s5, s2, 2 * kGPR, gb, j, X);
   tail_round<Lay, TR>(tile, 1 * kGPR + gb, Y, j);
-  load_tail<TB, TR>(rs, s5, s2, 3 * kGPR, gb, j, Y);
+  load_tail<TB, TR>(p, s5, s2, 3 * kGPR, gb, j, Y);
   tail_round<Lay, TR>(tile, 2 * kGPR + gb, X, j);
   next(X);   // the next stage's round 0 goes to X
   tail_round<Lay, TR>(tile, 3 * kGPR + gb, Y, j);
@@ -676,10 +725,9 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
   const int wave = threadIdx.x >> 6;
   int gb = wave * 16 + (lane >> 2);
   int j = lane & 3;
-  const __amdgpu_buffer_rsrc_t rs = coef_rsrc(p);
   Cbuf ca, cb;
-  if constexpr (!TR) load_coef<8, TB, TR>(rs, p.st[0], 0, gb, j, as8(ca));
-  else load_tail<TB, TR>(rs, p.st[1], p.st[0], 0, gb, j, ca);
+  if constexpr (!TR) load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(ca));
+  else load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, ca);
   __syncthreads();
   // The loop body covers two tiles: the first starts from ca, the second from
   // cb (where the first tile's last stage leaves the next tile's first round).
@@ -691,22 +739,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
       stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[0], ca, cb, gb, j,
-                                    [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[1], 0, gb, j, as8(d)); });
+                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[1], cb, ca, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], ca, cb, gb, j,
-                                   [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[3], p.st[4], 0, gb, j, d); });
+                                   [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], cb, ca, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[0], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], ca, cb, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], ca, cb, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[3], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[3], cb, ca, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[4], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], ca, cb, gb, j,
-                                    [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[1], p.st[0], 0, gb, j, d); });
+                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     __syncthreads();   // data waves have swapped the tile
     tix += gridDim.x;
@@ -714,22 +762,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
       stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[0], cb, ca, gb, j,
-                                    [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[1], 0, gb, j, as8(d)); });
+                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[1], ca, cb, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], cb, ca, gb, j,
-                                   [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[3], p.st[4], 0, gb, j, d); });
+                                   [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], ca, cb, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[0], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], cb, ca, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[2], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], cb, ca, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[3], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[3], ca, cb, gb, j,
-                                   [&](Cbuf& d) { load_coef<8, TB, TR>(rs, p.st[4], 0, gb, j, as8(d)); });
+                                   [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
       stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], cb, ca, gb, j,
-                                    [&](Cbuf& d) { load_tail<TB, TR>(rs, p.st[1], p.st[0], 0, gb, j, d); });
+                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     __syncthreads();   // data waves have swapped the tile
     tix += gridDim.x;
@@ -787,7 +835,7 @@ hipError_t launch_d(int d, const RowParams& p, int grid, hipStream_t st) {
 }  // namespace
 
 bool fast_path_supported(const Plan& pl, DT bdt) {
-  if (bdt != DT::F32 && bdt != DT::BF16) return false;
+  if (bdt != DT::F32 && bdt != DT::BF16 && bdt != DT::I8) return false;
   static const int r4096[] = {8, 8, 8, 8};
   static const int r5120[] = {8, 8, 8, 5, 2};
   const int* want = pl.d == 4096 ? r4096 : (pl.d == 5120 ? r5120 : nullptr);
@@ -798,19 +846,23 @@ bool fast_path_supported(const Plan& pl, DT bdt) {
   return true;
 }
 
-hipError_t launch_apply_fast(const Plan& pl, bool inverse, const void* blocks, DT bdt, const int8_t* signs,
-                             const void* x, int64_t ldx, DT io, void* y, int64_t ldy, int64_t rows,
-                             hipStream_t stream) {
+hipError_t launch_apply_fast(const Plan& pl, bool inverse, const void* blocks, DT bdt, const float* scales,
+                             const int8_t* signs, const void* x, int64_t ldx, DT io, void* y, int64_t ldy,
+                             int64_t rows, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  RowParams p = make_row_params(pl, inverse, blocks, nullptr, signs, x, ldx, io, y, ldy, rows);
+  RowParams p = make_row_params(pl, inverse, blocks, bdt == DT::I8 ? scales : nullptr, signs, x, ldx, io, y, ldy,
+                                rows);
   int64_t grid = cu_count();
   if (grid > p.ntiles) grid = p.ntiles;
   const int d = (int)pl.d;
-  if (io == DT::BF16)
-    return bdt == DT::F32 ? launch_d<uint16_t, float>(d, p, (int)grid, stream)
-                          : launch_d<uint16_t, uint16_t>(d, p, (int)grid, stream);
-  return bdt == DT::F32 ? launch_d<float, float>(d, p, (int)grid, stream)
-                        : launch_d<float, uint16_t>(d, p, (int)grid, stream);
+  if (io == DT::BF16) {
+    if (bdt == DT::F32) return launch_d<uint16_t, float>(d, p, (int)grid, stream);
+    if (bdt == DT::BF16) return launch_d<uint16_t, uint16_t>(d, p, (int)grid, stream);
+    return launch_d<uint16_t, int8_t>(d, p, (int)grid, stream);
+  }
+  if (bdt == DT::F32) return launch_d<float, float>(d, p, (int)grid, stream);
+  if (bdt == DT::BF16) return launch_d<float, uint16_t>(d, p, (int)grid, stream);
+  return launch_d<float, int8_t>(d, p, (int)grid, stream);
 }
 
 }  // namespace harp

@@ -217,7 +217,7 @@ hipError_t launch_apply_rows(const Plan& pl, bool inverse, const void* blocks, D
   if (in_dt == out_dt && row_kernel != 3 && row_path_supported(pl, in_dt, blocks, signs, x, ldx, y, ldy)) {
     static const int roles = env_int("HARP_ROW_ROLES", 0);
     if ((row_kernel == 0 || row_kernel == 4) && fast_path_supported(pl, bdt))
-      return launch_apply_fast(pl, inverse, blocks, bdt, signs, x, ldx, in_dt, y, ldy, rows, stream);
+      return launch_apply_fast(pl, inverse, blocks, bdt, scales, signs, x, ldx, in_dt, y, ldy, rows, stream);
     const bool valu = row_kernel == 2 || (row_kernel == 0 && bdt == DT::I8);
     if (valu)
       return launch_apply_valu(pl, inverse, blocks, bdt, scales, signs, x, ldx, in_dt, y, ldy, rows, roles, stream);

@@ -407,7 +407,10 @@ __device__ __forceinline__ void chunk_src(const DecFixed& p, int n, int k, int64
   constexpr int begin = Rn::coef_off(I) * esz / 16;
   const int kk = k - begin;
   if (p.first) {
-    constexpr int cpb = b * b * esz / 16;         // chunks per block
+    // chunks per block: the host takes this kernel for a run that starts at
+    // digit 0 only when each block is whole 16-byte chunks; the guard only
+    // keeps the constant nonzero in instantiations that never get here
+    constexpr int cpb = b * b * esz / 16 > 0 ? b * b * esz / 16 : 1;
     const int q = kk / cpb;
     const int w = kk - q * cpb;
     *src_byte = ((int64_t)p.blk_off[I] + (int64_t)(q * p.inner + n) * (b * b)) * esz + w * 16;

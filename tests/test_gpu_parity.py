@@ -157,22 +157,46 @@ def test_apply_and_inverse_small(name, blk):
 
 
 @pytest.mark.parametrize("name", ["cayley4096_bf16", "mixed5120_bf16"])
-def test_apply_full_size_sampled(name):
+@pytest.mark.parametrize("blk", ["f32", "bf16", "i8"])
+def test_apply_full_size_sampled(name, blk):
+    print(f"\n[case] full size {name} blk={blk}", flush=True)
     w = _case(name)
     sch, d, io = w["schedule"], w["d"], w["io"]
-    blocks_g, _ = gpu_blocks(api, sch, d, w["theta"], w["gauss"], "f32")
+    blocks_g, scales_g = gpu_blocks(api, sch, d, w["theta"], w["gauss"], blk)
     sg = signs_dev(w["signs"])
     xd = to_dev(w["x"], io)
-    y = api.harp_apply(sch, d, blocks_g, None, sg, xd)
-    xr = api.harp_apply_inverse(sch, d, blocks_g, None, sg, y)
+    y = api.harp_apply(sch, d, blocks_g, scales_g, sg, xd)
+    xr = api.harp_apply_inverse(sch, d, blocks_g, scales_g, sg, y)
     torch.cuda.synchronize()
     n = w["rows"]
     idx = np.unique(np.concatenate([[0, 1, n - 1], SAMPLE.choice(n, 96, replace=False)]))
-    blocks_o, y_ref = _apply_refs(w, "f32", w["x"][idx].astype(np.float64))
+    blocks_o, y_ref = _apply_refs(w, blk, w["x"][idx].astype(np.float64))
     y_s = from_dev(y[torch.from_numpy(idx).cuda()])
-    assert_rows_close(y_s, y_ref, TOL[io], f"{name} full forward")
+    assert_rows_close(y_s, y_ref, TOL[io], f"{name}/{blk} full forward")
     x_ref = O.apply_inverse(y_s, sch, blocks_o, w["signs"].astype(float))
-    assert_rows_close(from_dev(xr[torch.from_numpy(idx).cuda()]), x_ref, TOL[io], f"{name} full inverse")
+    assert_rows_close(from_dev(xr[torch.from_numpy(idx).cuda()]), x_ref, TOL[io], f"{name}/{blk} full inverse")
+
+
+@pytest.mark.parametrize("name", ["cayley4096_bf16", "mixed5120_bf16"])
+@pytest.mark.parametrize("blk", ["bf16", "i8"])
+def test_apply_stored_blocks_fp32_rows(name, blk):
+    # fp32 rows through the schedule-specialised kernels with bf16 and int8
+    # blocks: the blocks' stored values decoded in the kernel must give the
+    # oracle's result on the same stored values to fp32 accuracy, both ways
+    print(f"\n[case] fp32 rows {name} blk={blk}", flush=True)
+    w = _case(name, 21)
+    sch, d = w["schedule"], w["d"]
+    x = w["x"].astype(np.float64)
+    blocks_g, scales_g = gpu_blocks(api, sch, d, w["theta"], w["gauss"], blk)
+    sg = signs_dev(w["signs"])
+    y = api.harp_apply(sch, d, blocks_g, scales_g, sg, to_dev(w["x"], "f32"))
+    torch.cuda.synchronize()
+    blocks_o, y_ref = _apply_refs(w, blk, x)
+    assert_rows_close(from_dev(y), y_ref, TOL["f32"], f"{name}/{blk} fp32 forward")
+    xr = api.harp_apply_inverse(sch, d, blocks_g, scales_g, sg, y)
+    torch.cuda.synchronize()
+    x_ref = O.apply_inverse(from_dev(y), sch, blocks_o, w["signs"].astype(float))
+    assert_rows_close(from_dev(xr), x_ref, TOL["f32"], f"{name}/{blk} fp32 inverse")
 
 
 def test_roundtrip_fp32_rows_is_identity():
