@@ -326,13 +326,14 @@ def vjp_main(args) -> int:
     ms_theta = timed(lambda: api.harp_theta_vjp(sch, d, th, gs, db, dt))
     m = len(sch)
     rd = rows * d
-    nchunk = (ws.numel() - 4 * rd * ((m - 1) + (2 if m > 1 else 0))) // (4 * nblk)
+    # fp32 block-gradient partial sums in the workspace: one slot per backward workgroup
+    nslot = (ws.numel() - 4 * rd * ((m - 1) + (2 if m > 1 else 0))) // (4 * nblk)
     fwd = rd * (eb + 4) + (m - 2) * rd * 8 if m > 1 else 0
     if m > 1:
         bwd = rd * (eb + 4 + 4) + (m - 2) * rd * 12 + rd * (4 + eb + eb)
     else:
         bwd = rd * 3 * eb
-    red = nchunk * nblk * 4 * 2 + nblk * 4
+    red = nslot * nblk * 4 * 2 + nblk * 4
     moved = fwd + bwd + red
     # dx = M^T dy is the inverse transform of dy for orthogonal blocks: the
     # reverse mode's dx agrees with harp_apply_inverse to rounding (parity
@@ -355,7 +356,7 @@ def vjp_main(args) -> int:
         "achieved_GBps_on_design_bytes": round(moved / (ms_vjp * 1e-3) / 1e9, 1),
         "io_bytes_x_dy_dx": 3 * rd * eb,
         "ms_theta_vjp": round(ms_theta, 4),
-        "chunks": int(nchunk),
+        "partial_slots": int(nslot),
         "dx_vs_inverse_max_row_rel_l2": par,
     }
     print(json.dumps(line), flush=True)
@@ -444,6 +445,8 @@ def main() -> int:
                          "every launch")
     ap.add_argument("--single", action="store_true",
                     help="the named workload only (the default workload otherwise brings the d = 5120 one along)")
+    ap.add_argument("--fp32-intermediates", action="store_true",
+                    help="two-sided workload: keep the passes' intermediates in an fp32 workspace")
     ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize", "vjp"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -515,9 +518,16 @@ def throughput(name: str, args, with_cpu: bool) -> dict:
         sv_s = torch.from_numpy(w["signs_v"]).cuda()
 
         # the rotation as planned for this workload: bf16 between the passes,
-        # in place in the output (no workspace)
+        # in place in the output (no workspace); --fp32-intermediates: the
+        # binding's default, fp32 between the passes in a workspace allocated
+        # once here
+        ws = None
+        if args.fp32_intermediates:
+            ws = torch.empty(api.harp_rotate_weight_workspace(w["d_out"], d), dtype=torch.uint8, device="cuda")
+
         def step():
-            api.harp_rotate_weight(w["su"], bu, scu, su_s, sch, bv, scv, sv_s, x, y, fp32_intermediates=False)
+            api.harp_rotate_weight(w["su"], bu, scu, su_s, sch, bv, scv, sv_s, x, y, workspace=ws,
+                                   fp32_intermediates=ws is not None)
         alg_bytes = rows * d * eb * 2
         # b_t FMAs per element per stage, both sides
         alg_flops = 2 * rows * d * (sum(sch) + sum(w["su"]))
@@ -585,7 +595,8 @@ def throughput(name: str, args, with_cpu: bool) -> dict:
         roundtrip = float(row_rel_l2(xb.float().cpu().numpy(), x.float().cpu().numpy()).max())
 
     unit = {"apply": "rows/s", "rht": "rows/s", "two_sided": "weights/s"}[wl.kind]
-    traffic = None if args.copy_calibration else traffic_from_profile(name, args.blk)
+    # counter records are taken on each workload's default configuration
+    traffic = None if (args.copy_calibration or args.fp32_intermediates) else traffic_from_profile(name, args.blk)
     line = {
         "metric": "HARP apply rows/s + achieved HBM GB/s (% of peak), d=4096/5120 bf16",
         "value": round(value, 1),
@@ -621,7 +632,7 @@ def throughput(name: str, args, with_cpu: bool) -> dict:
     if not args.copy_calibration:
         line["copy_ceiling"] = copy_ceiling(x, y, stream, achieved)
     if wl.kind == "two_sided":
-        line["config"]["intermediates"] = "bf16, in place"
+        line["config"]["intermediates"] = "fp32 workspace" if args.fp32_intermediates else "bf16, in place"
     if with_cpu and not args.copy_calibration:
         line["cpu_baseline"] = cpu_baseline(w, args.blk, y)
     return line
