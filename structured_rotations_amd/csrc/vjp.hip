@@ -60,6 +60,7 @@ struct VjpArgs {
   int64_t n_blk;
   int vec1;                  // backward: stride-1 stage whose rows of x_t, g_{t+1} and the output
                              // allow 16-byte (8-byte for 4 bf16) accesses of a group's coordinates
+  VjpStage st2;              // fused last pair: the last stage (st is the one before it)
 };
 
 template <typename TB>
@@ -309,6 +310,165 @@ __global__ void __launch_bounds__(kBwdThreads) vjp_bwd_kernel(VjpArgs a) {
   }
 }
 
+// The last two stages in one backward launch, when both are radix 8 (digit
+// strides 8 and 1).  Their groups then live in units of 64 consecutive
+// coordinates c = 64 u + 8 a + b: stage m-2 mixes a (group 8u + b), stage m-1
+// mixes b (group 8u + a).  A wave owns one unit over a chunk of rows, lane
+// 8a + b owning coordinate c, and per row:
+//   x_{m-1}[a,b] = sum_k B_{m-2}[a][k] x_{m-2}[k,b]     (recomputed: the
+//                                                        forward never stores it)
+//   g_{m-1}[a,b] = sum_r B_{m-1}[r][b] dy[a,r]
+//   g_{m-2}[a,b] = sum_r B_{m-2}[r][a] g_{m-1}[r,b]
+// with the gradient rows dB_{m-1}[8u+a][b][.] += dy[a,b] x_{m-1}[a,.] and
+// dB_{m-2}[8u+b][a][.] += g_{m-1}[a,b] x_{m-2}[.,b] in registers; the values
+// of a column (same b) or a row (same a) of the unit reach the lane by
+// cross-lane reads.  Against two stage launches it reads x_{m-2} and dy once
+// and writes g_{m-2} once, and the forward saves writing x_{m-1}.  Rows are
+// taken kPairRows at a time so that their loads are in flight together.
+constexpr int kPairRows = 4;
+
+template <typename TB, typename TX, typename TG, typename TO>
+__global__ void __launch_bounds__(kBwdThreads, 3) vjp_bwd_pair88_kernel(VjpArgs a) {
+  __shared__ float red[kBwdWaves - 1][16][64];
+  // per wave and row in flight: x_{m-2} by column (b-major), x_{m-1} and dy
+  // by row (a-major), g_{m-1} by column; a lane reads its 8 values as two
+  // 16-byte words
+  __shared__ __align__(16) float xch[kBwdWaves][kPairRows][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nunit = (int)(a.d / 64);
+  const int u = (int)(blockIdx.x % nunit);
+  const int cb = (int)(blockIdx.x / nunit);
+  const int chunk = cb * kBwdWaves + wave;
+  const int ia = lane >> 3, ib = lane & 7;
+  const int tl = ib * 8 + ia;   // the lane's slot in a b-major array
+  const int64_t c = (int64_t)u * 64 + lane;
+  const int g0 = u * 8 + ib;   // stage m-2 group
+  const int g1 = u * 8 + ia;   // stage m-1 group
+  float brow[8], bcol[8], b1col[8];
+  {
+    const TB* p0 = static_cast<const TB*>(a.blocks) + a.st.blk_off + (int64_t)g0 * 64;
+    const TB* p1 = static_cast<const TB*>(a.blocks) + a.st2.blk_off + (int64_t)g1 * 64;
+    const float s0 = sizeof(TB) == 1 ? a.scales[a.st.grp_off + g0] : 1.0f;
+    const float s1 = sizeof(TB) == 1 ? a.scales[a.st2.grp_off + g1] : 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      brow[k] = coef_at<TB>(p0, ia * 8 + k) * s0;
+      bcol[k] = coef_at<TB>(p0, k * 8 + ia) * s0;
+      b1col[k] = coef_at<TB>(p1, k * 8 + ib) * s1;
+    }
+  }
+  const float xs = a.x_sign ? (float)a.signs[c] : 1.0f;
+  const float os = a.o_sign ? (float)a.signs[c] : 1.0f;
+  float acc1[8], acc0[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    acc1[k] = 0.0f;
+    acc0[k] = 0.0f;
+  }
+  const int64_t r0 = (int64_t)chunk * a.rpc;
+  const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
+  const TX* xin = static_cast<const TX*>(a.xin) + c;
+  const TG* gin = static_cast<const TG*>(a.gin) + c;
+  TO* out = static_cast<TO*>(a.out);
+  float(*buf)[4][64] = xch[wave];
+  auto read8 = [&](const float* p, float (&v)[8]) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  };
+  // the wave's own LDS writes before its cross-lane reads of them
+  auto lds_wait = [] {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+  };
+  for (int64_t row0 = r0; row0 < r1; row0 += kPairRows) {
+    float xv[kPairRows], gv[kPairRows];
+#pragma unroll
+    for (int i = 0; i < kPairRows; ++i) {
+      // rows past the chunk re-read its last row; their results are dropped
+      const int64_t row = row0 + i < r1 ? row0 + i : r1 - 1;
+      xv[i] = ld_t<TX>(xin + row * a.ldx, 0) * xs;
+      gv[i] = ld_t<TG>(gin + row * a.ldg, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPairRows; ++i) {
+      buf[i][0][tl] = xv[i];
+      buf[i][2][lane] = gv[i];
+    }
+    lds_wait();
+    float xcol[kPairRows][8], x1[kPairRows];
+#pragma unroll
+    for (int i = 0; i < kPairRows; ++i) {
+      read8(&buf[i][0][ib * 8], xcol[i]);
+      float s1 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s1 = fmaf(brow[k], xcol[i][k], s1);
+      x1[i] = s1;
+      buf[i][1][lane] = s1;
+    }
+    lds_wait();
+    float g1v[kPairRows];
+#pragma unroll
+    for (int i = 0; i < kPairRows; ++i) {
+      const bool live = row0 + i < r1;
+      float x1row[8], g2row[8];
+      read8(&buf[i][1][ia * 8], x1row);
+      read8(&buf[i][2][ia * 8], g2row);
+      float g = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (live) acc1[k] = fmaf(gv[i], x1row[k], acc1[k]);
+        g = fmaf(b1col[k], g2row[k], g);
+      }
+      g1v[i] = g;
+      buf[i][3][tl] = g;
+    }
+    (void)x1;
+    lds_wait();
+#pragma unroll
+    for (int i = 0; i < kPairRows; ++i) {
+      const bool live = row0 + i < r1;
+      float g1col[8];
+      read8(&buf[i][3][ib * 8], g1col);
+      float o = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (live) acc0[k] = fmaf(g1v[i], xcol[i][k], acc0[k]);
+        o = fmaf(bcol[k], g1col[k], o);
+      }
+      if (live && out != nullptr) st_t<TO>(out + (row0 + i) * a.ldo, c, o * os);
+    }
+    // the next rows overwrite this wave's slots only after these reads
+    lds_wait();
+  }
+  // fixed-order sum over the workgroup's row chunks, as in vjp_bwd_kernel
+  if (wave > 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      red[wave - 1][k][lane] = acc1[k];
+      red[wave - 1][8 + k][lane] = acc0[k];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < kBwdWaves - 1; ++w)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc1[k] += red[w][k][lane];
+        acc0[k] += red[w][8 + k][lane];
+      }
+    float* pp = a.partial + (int64_t)cb * a.n_blk;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pp[a.st2.blk_off + (int64_t)g1 * 64 + ib * 8 + k] = acc1[k];
+      pp[a.st.blk_off + (int64_t)g0 * 64 + ia * 8 + k] = acc0[k];
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kVjpThreads) vjp_reduce_kernel(const float* partial, int nslot, int64_t n_blk,
                                                                  float* dblocks) {
   const int64_t i = (int64_t)blockIdx.x * kVjpThreads + threadIdx.x;
@@ -377,6 +537,29 @@ hipError_t launch_stage_any(bool fwd, DT bdt, const VjpArgs& a, hipStream_t st) 
   return launch_stage_b<int8_t>(fwd, a, st);
 }
 
+template <typename TB>
+hipError_t launch_pair(const VjpArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.d / 64) * (a.nchunk / kBwdWaves)));
+  using F = float;
+  using H16 = uint16_t;
+  // x_{m-2} and the output are the caller's rows only when m = 2
+  if (!a.x_bf16 && !a.g_bf16 && !a.o_bf16)
+    hipLaunchKernelGGL((vjp_bwd_pair88_kernel<TB, F, F, F>), grid, dim3(kBwdThreads), 0, st, a);
+  else if (!a.x_bf16 && a.g_bf16 && !a.o_bf16)
+    hipLaunchKernelGGL((vjp_bwd_pair88_kernel<TB, F, H16, F>), grid, dim3(kBwdThreads), 0, st, a);
+  else if (a.x_bf16 && a.g_bf16 && a.o_bf16)
+    hipLaunchKernelGGL((vjp_bwd_pair88_kernel<TB, H16, H16, H16>), grid, dim3(kBwdThreads), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_any(DT bdt, const VjpArgs& a, hipStream_t st) {
+  if (bdt == DT::F32) return launch_pair<float>(a, st);
+  if (bdt == DT::BF16) return launch_pair<uint16_t>(a, st);
+  return launch_pair<int8_t>(a, st);
+}
+
 }  // namespace
 
 int64_t vjp_workspace_bytes(const Plan& pl, int64_t rows) {
@@ -420,8 +603,11 @@ hipError_t launch_apply_vjp(const Plan& pl, const void* blocks, DT bdt, const fl
   base.n_blk = pl.n_blk;
   base.partial = part;
 
-  // forward: x_{t+1} = S_t x_t for t = 0 .. m-2
-  for (int t = 0; t + 1 < pl.m; ++t) {
+  // last two stages radix 8: one fused backward launch, which recomputes
+  // x_{m-1} itself
+  const bool pair = pl.m >= 2 && pl.radix[pl.m - 1] == 8 && pl.radix[pl.m - 2] == 8;
+  // forward: x_{t+1} = S_t x_t for t = 0 .. m-2 (m-3 with the fused pair)
+  for (int t = 0; t + 1 < pl.m - (pair ? 1 : 0); ++t) {
     VjpArgs a = base;
     a.st = stage_of(t);
     a.xin = t == 0 ? x : static_cast<const void*>(acts + (int64_t)(t - 1) * rd);
@@ -434,7 +620,33 @@ hipError_t launch_apply_vjp(const Plan& pl, const void* blocks, DT bdt, const fl
     if (e != hipSuccess) return e;
   }
   // backward: t = m-1 .. 0
-  for (int t = pl.m - 1; t >= 0; --t) {
+  int t_top = pl.m - 1;
+  if (pair) {
+    VjpArgs a = base;
+    const int t = pl.m - 2;
+    a.st = stage_of(t);
+    a.st2 = stage_of(t + 1);
+    a.gin = dy;
+    a.ldg = lddy;
+    a.g_bf16 = bf;
+    a.xin = t == 0 ? x : static_cast<const void*>(acts + (int64_t)(t - 1) * rd);
+    a.ldx = t == 0 ? ldx : pl.d;
+    a.x_bf16 = t == 0 ? bf : 0;
+    a.x_sign = (t == 0 && signs != nullptr) ? 1 : 0;
+    if (t == 0) {
+      a.out = dx;
+      a.ldo = lddx;
+      a.o_bf16 = bf;
+      a.o_sign = signs != nullptr ? 1 : 0;
+    } else {
+      a.out = gbuf + rd;   // the buffer the step for stage m-2 writes (step 1: gbuf[1])
+      a.ldo = pl.d;
+    }
+    hipError_t e = launch_pair_any(bdt, a, stream);
+    if (e != hipSuccess) return e;
+    t_top = pl.m - 3;
+  }
+  for (int t = t_top; t >= 0; --t) {
     VjpArgs a = base;
     a.st = stage_of(t);
     const int k = pl.m - 1 - t;   // backward step

@@ -182,3 +182,29 @@ def test_vjp_strided_rows(sch, d, io, pad):
     if pad:
         base = dx.as_strided((rows, pad), (d + pad, 1), d)   # the pad columns beside each row
         assert bool((base.float() == 7.0).all()), "dx written outside its rows"
+
+
+@pytest.mark.parametrize("sch,d", [((8, 8), 64), ((3, 8, 8), 192), ((2, 2, 8, 8), 256)])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("blk", ["f32", "i8"])
+def test_vjp_fused_last_pair(sch, d, io, blk):
+    """Schedules ending in two radix-8 stages take the fused backward launch
+    for that pair (with m = 2 it reads x and writes dx itself, signs on both
+    sides); row counts that leave partial row groups and empty chunks."""
+    print(f"\n[case] vjp fused pair {sch} io={io} blk={blk}", flush=True)
+    g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 400 + d)
+    theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
+    gauss = I.gauss_mats(g_gauss, sch)
+    signs = I.rademacher(g_sign, d)
+    for rows in (1, 13, 517):
+        x = g_data.standard_normal((rows, d)).astype(np.float32)
+        if io == "bf16":
+            x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+        dy = _dy(rows, d, io, 10 + rows)
+        blocks_g, scales_g = gpu_blocks(api, sch, d, theta, gauss, blk)
+        dx, db = api.harp_apply_vjp(sch, d, blocks_g, scales_g, signs_dev(signs), to_dev(x, io), to_dev(dy, io))
+        torch.cuda.synchronize()
+        blocks_o = oracle_blocks(sch, d, theta, gauss, blk)
+        rdx, rdb = O.apply_vjp(x.astype(np.float64), sch, blocks_o, signs.astype(float), dy.astype(np.float64))
+        assert_rows_close(from_dev(dx), rdx, TOL[io], f"{sch}/{io}/{blk}/{rows} dx")
+        assert_groups_close(db.cpu().numpy().astype(np.float64), rdb, sch, DB_TOL, f"{sch}/{io}/{blk}/{rows} dB")
