@@ -471,6 +471,15 @@ def main() -> int:
                                              "kernel_ms_mean", "kernel_ms_median", "kernel_ms_p10_p90",
                                              "kernel_ms_mean_flushed", "alg_bytes_per_launch", "compute",
                                              "roundtrip_max_row_rel_l2", "copy_ceiling")}
+        if args.blk == "f32":
+            # the stored-block options of the same d = 4096 workload (a9): the
+            # blocks themselves are rounded, so these lines measure a
+            # different operator and stay beside the fp32 headline
+            for b in ("bf16", "i8"):
+                sub = throughput(DEFAULT_WORKLOAD, argparse.Namespace(**{**vars(args), "blk": b}), with_cpu=False)
+                line[f"blocks_{b}"] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "roofline", "kernel_ms_mean",
+                                                           "kernel_ms_median", "kernel_ms_mean_flushed",
+                                                           "roundtrip_max_row_rel_l2")}
     print(json.dumps(line), flush=True)
     return 0
 
