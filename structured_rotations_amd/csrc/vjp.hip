@@ -310,74 +310,93 @@ __global__ void __launch_bounds__(kBwdThreads) vjp_bwd_kernel(VjpArgs a) {
   }
 }
 
-// The last two stages in one backward launch, when both are radix 8 (digit
-// strides 8 and 1).  Their groups then live in units of 64 consecutive
-// coordinates c = 64 u + 8 a + b: stage m-2 mixes a (group 8u + b), stage m-1
-// mixes b (group 8u + a).  A wave owns one unit over a chunk of rows, lane
-// 8a + b owning coordinate c, and per row:
+// The last two stages in one backward launch.  With radices BA (stage m-2,
+// digit stride BB) and BB (stage m-1, stride 1), their groups live in units
+// of BA * BB consecutive coordinates c = U u + BB a + b (U = BA * BB): stage
+// m-2 mixes a (group BB u + b), stage m-1 mixes b (group BA u + a).  A wave
+// owns 64 / U units over a chunk of rows, lane U v + BB a + b owning
+// coordinate c of its v-th unit, and per row:
 //   x_{m-1}[a,b] = sum_k B_{m-2}[a][k] x_{m-2}[k,b]     (recomputed: the
 //                                                        forward never stores it)
 //   g_{m-1}[a,b] = sum_r B_{m-1}[r][b] dy[a,r]
 //   g_{m-2}[a,b] = sum_r B_{m-2}[r][a] g_{m-1}[r,b]
-// with the gradient rows dB_{m-1}[8u+a][b][.] += dy[a,b] x_{m-1}[a,.] and
-// dB_{m-2}[8u+b][a][.] += g_{m-1}[a,b] x_{m-2}[.,b] in registers; the values
-// of a column (same b) or a row (same a) of the unit reach the lane by
-// cross-lane reads.  Against two stage launches it reads x_{m-2} and dy once
-// and writes g_{m-2} once, and the forward saves writing x_{m-1}.  Rows are
+// with the gradient rows dB_{m-1}[BA u+a][b][.] += dy[a,b] x_{m-1}[a,.] and
+// dB_{m-2}[BB u+b][a][.] += g_{m-1}[a,b] x_{m-2}[.,b] in registers.  The
+// values of a column (same b) or a row (same a) of a unit reach the lane
+// through the wave's own LDS slots (two 16-byte words for radix-8 rows and
+// columns).  Against two stage launches it reads x_{m-2} and dy once and
+// writes g_{m-2} once, and the forward saves writing x_{m-1}.  Rows are
 // taken kPairRows at a time so that their loads are in flight together.
 constexpr int kPairRows = 4;
 
-template <typename TB, typename TX, typename TG, typename TO>
-__global__ void __launch_bounds__(kBwdThreads, 3) vjp_bwd_pair88_kernel(VjpArgs a) {
-  __shared__ float red[kBwdWaves - 1][16][64];
+template <int N>
+__device__ __forceinline__ void read_n(const float* p, float (&v)[N]) {
+  if constexpr (N == 8) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = p[k];
+  }
+}
+
+template <int BA, int BB, typename TB, typename TX, typename TG, typename TO>
+__global__ void __launch_bounds__(kBwdThreads, 3) vjp_bwd_pair_kernel(VjpArgs a) {
+  constexpr int U = BA * BB;
+  constexpr int UPW = 64 / U;    // units per wave
+  __shared__ float red[kBwdWaves - 1][BA + BB][64];
   // per wave and row in flight: x_{m-2} by column (b-major), x_{m-1} and dy
-  // by row (a-major), g_{m-1} by column; a lane reads its 8 values as two
-  // 16-byte words
+  // by row (a-major), g_{m-1} by column
   __shared__ __align__(16) float xch[kBwdWaves][kPairRows][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nunit = (int)(a.d / 64);
-  const int u = (int)(blockIdx.x % nunit);
-  const int cb = (int)(blockIdx.x / nunit);
+  const int64_t nunit = a.d / U;
+  const int64_t nset = (nunit + UPW - 1) / UPW;   // unit sets (one per wave and chunk)
+  const int64_t set = (int64_t)blockIdx.x % nset;
+  const int cb = (int)((int64_t)blockIdx.x / nset);
   const int chunk = cb * kBwdWaves + wave;
-  const int ia = lane >> 3, ib = lane & 7;
-  const int tl = ib * 8 + ia;   // the lane's slot in a b-major array
-  const int64_t c = (int64_t)u * 64 + lane;
-  const int g0 = u * 8 + ib;   // stage m-2 group
-  const int g1 = u * 8 + ia;   // stage m-1 group
-  float brow[8], bcol[8], b1col[8];
+  const int v = lane / U, li = lane - v * U;
+  const int64_t unit = set * UPW + v;
+  // lanes past the last unit only pass values along (with one unit per
+  // wave, every lane has one)
+  const bool valid = UPW == 1 || (v < UPW && unit < nunit);
+  // lanes without a unit read unit 0's slots and write only to their own
+  // lane's slot, which no unit uses (every index below stays under 64)
+  const int ia = valid ? li / BB : 0, ib = valid ? li - (li / BB) * BB : 0;
+  const int ubase = valid ? v * U : 0;
+  const int tl = valid ? ubase + ib * BA + ia : lane;   // the lane's slot in a b-major unit
+  const int64_t c = valid ? unit * U + li : 0;
+  const int64_t g0 = valid ? unit * BB + ib : 0;  // stage m-2 group
+  const int64_t g1 = valid ? unit * BA + ia : 0;  // stage m-1 group
+  float brow[BA], bcol[BA], b1col[BB];
   {
-    const TB* p0 = static_cast<const TB*>(a.blocks) + a.st.blk_off + (int64_t)g0 * 64;
-    const TB* p1 = static_cast<const TB*>(a.blocks) + a.st2.blk_off + (int64_t)g1 * 64;
+    const TB* p0 = static_cast<const TB*>(a.blocks) + a.st.blk_off + g0 * BA * BA;
+    const TB* p1 = static_cast<const TB*>(a.blocks) + a.st2.blk_off + g1 * BB * BB;
     const float s0 = sizeof(TB) == 1 ? a.scales[a.st.grp_off + g0] : 1.0f;
     const float s1 = sizeof(TB) == 1 ? a.scales[a.st2.grp_off + g1] : 1.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      brow[k] = coef_at<TB>(p0, ia * 8 + k) * s0;
-      bcol[k] = coef_at<TB>(p0, k * 8 + ia) * s0;
-      b1col[k] = coef_at<TB>(p1, k * 8 + ib) * s1;
+    for (int k = 0; k < BA; ++k) {
+      brow[k] = coef_at<TB>(p0, ia * BA + k) * s0;
+      bcol[k] = coef_at<TB>(p0, k * BA + ia) * s0;
     }
+#pragma unroll
+    for (int k = 0; k < BB; ++k) b1col[k] = coef_at<TB>(p1, k * BB + ib) * s1;
   }
   const float xs = a.x_sign ? (float)a.signs[c] : 1.0f;
   const float os = a.o_sign ? (float)a.signs[c] : 1.0f;
-  float acc1[8], acc0[8];
+  float acc1[BB], acc0[BA];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    acc1[k] = 0.0f;
-    acc0[k] = 0.0f;
-  }
+  for (int k = 0; k < BB; ++k) acc1[k] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < BA; ++k) acc0[k] = 0.0f;
   const int64_t r0 = (int64_t)chunk * a.rpc;
   const int64_t r1 = r0 + a.rpc < a.rows ? r0 + a.rpc : a.rows;
   const TX* xin = static_cast<const TX*>(a.xin) + c;
   const TG* gin = static_cast<const TG*>(a.gin) + c;
   TO* out = static_cast<TO*>(a.out);
   float(*buf)[4][64] = xch[wave];
-  auto read8 = [&](const float* p, float (&v)[8]) {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
-    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-  };
   // the wave's own LDS writes before its cross-lane reads of them
   auto lds_wait = [] {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -389,8 +408,8 @@ __global__ void __launch_bounds__(kBwdThreads, 3) vjp_bwd_pair88_kernel(VjpArgs 
     for (int i = 0; i < kPairRows; ++i) {
       // rows past the chunk re-read its last row; their results are dropped
       const int64_t row = row0 + i < r1 ? row0 + i : r1 - 1;
-      xv[i] = ld_t<TX>(xin + row * a.ldx, 0) * xs;
-      gv[i] = ld_t<TG>(gin + row * a.ldg, 0);
+      xv[i] = valid ? ld_t<TX>(xin + row * a.ldx, 0) * xs : 0.0f;
+      gv[i] = valid ? ld_t<TG>(gin + row * a.ldg, 0) : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < kPairRows; ++i) {
@@ -398,43 +417,41 @@ __global__ void __launch_bounds__(kBwdThreads, 3) vjp_bwd_pair88_kernel(VjpArgs 
       buf[i][2][lane] = gv[i];
     }
     lds_wait();
-    float xcol[kPairRows][8], x1[kPairRows];
+    float xcol[kPairRows][BA];
 #pragma unroll
     for (int i = 0; i < kPairRows; ++i) {
-      read8(&buf[i][0][ib * 8], xcol[i]);
+      read_n<BA>(&buf[i][0][ubase + ib * BA], xcol[i]);
       float s1 = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) s1 = fmaf(brow[k], xcol[i][k], s1);
-      x1[i] = s1;
+      for (int k = 0; k < BA; ++k) s1 = fmaf(brow[k], xcol[i][k], s1);
       buf[i][1][lane] = s1;
     }
     lds_wait();
     float g1v[kPairRows];
 #pragma unroll
     for (int i = 0; i < kPairRows; ++i) {
-      const bool live = row0 + i < r1;
-      float x1row[8], g2row[8];
-      read8(&buf[i][1][ia * 8], x1row);
-      read8(&buf[i][2][ia * 8], g2row);
+      const bool live = valid && row0 + i < r1;
+      float x1row[BB], g2row[BB];
+      read_n<BB>(&buf[i][1][ubase + ia * BB], x1row);
+      read_n<BB>(&buf[i][2][ubase + ia * BB], g2row);
       float g = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < BB; ++k) {
         if (live) acc1[k] = fmaf(gv[i], x1row[k], acc1[k]);
         g = fmaf(b1col[k], g2row[k], g);
       }
       g1v[i] = g;
       buf[i][3][tl] = g;
     }
-    (void)x1;
     lds_wait();
 #pragma unroll
     for (int i = 0; i < kPairRows; ++i) {
-      const bool live = row0 + i < r1;
-      float g1col[8];
-      read8(&buf[i][3][ib * 8], g1col);
+      const bool live = valid && row0 + i < r1;
+      float g1col[BA];
+      read_n<BA>(&buf[i][3][ubase + ib * BA], g1col);
       float o = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < BA; ++k) {
         if (live) acc0[k] = fmaf(g1v[i], xcol[i][k], acc0[k]);
         o = fmaf(bcol[k], g1col[k], o);
       }
@@ -446,27 +463,30 @@ __global__ void __launch_bounds__(kBwdThreads, 3) vjp_bwd_pair88_kernel(VjpArgs 
   // fixed-order sum over the workgroup's row chunks, as in vjp_bwd_kernel
   if (wave > 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      red[wave - 1][k][lane] = acc1[k];
-      red[wave - 1][8 + k][lane] = acc0[k];
-    }
+    for (int k = 0; k < BB; ++k) red[wave - 1][k][lane] = acc1[k];
+#pragma unroll
+    for (int k = 0; k < BA; ++k) red[wave - 1][BB + k][lane] = acc0[k];
   }
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 0 && valid) {
 #pragma unroll
-    for (int w = 0; w < kBwdWaves - 1; ++w)
+    for (int w = 0; w < kBwdWaves - 1; ++w) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc1[k] += red[w][k][lane];
-        acc0[k] += red[w][8 + k][lane];
-      }
+      for (int k = 0; k < BB; ++k) acc1[k] += red[w][k][lane];
+#pragma unroll
+      for (int k = 0; k < BA; ++k) acc0[k] += red[w][BB + k][lane];
+    }
     float* pp = a.partial + (int64_t)cb * a.n_blk;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pp[a.st2.blk_off + (int64_t)g1 * 64 + ib * 8 + k] = acc1[k];
-      pp[a.st.blk_off + (int64_t)g0 * 64 + ia * 8 + k] = acc0[k];
-    }
+    for (int k = 0; k < BB; ++k) pp[a.st2.blk_off + g1 * BB * BB + ib * BB + k] = acc1[k];
+#pragma unroll
+    for (int k = 0; k < BA; ++k) pp[a.st.blk_off + g0 * BA * BA + ia * BA + k] = acc0[k];
   }
+}
+
+// Last-stage pairs compiled in (radices of stages m-2, m-1).
+__host__ __device__ constexpr bool pair_compiled(int ba, int bb) {
+  return (ba == 8 && bb == 8) || (ba == 5 && bb == 2) || (ba == 3 && bb == 3);
 }
 
 __global__ void __launch_bounds__(kVjpThreads) vjp_reduce_kernel(const float* partial, int nslot, int64_t n_blk,
@@ -537,21 +557,31 @@ hipError_t launch_stage_any(bool fwd, DT bdt, const VjpArgs& a, hipStream_t st) 
   return launch_stage_b<int8_t>(fwd, a, st);
 }
 
-template <typename TB>
-hipError_t launch_pair(const VjpArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.d / 64) * (a.nchunk / kBwdWaves)));
+template <int BA, int BB, typename TB>
+hipError_t launch_pair_ab(const VjpArgs& a, hipStream_t st) {
+  constexpr int U = BA * BB, UPW = 64 / U;
+  const int64_t nset = (a.d / U + UPW - 1) / UPW;
+  const dim3 grid((unsigned)(nset * (a.nchunk / kBwdWaves)));
   using F = float;
   using H16 = uint16_t;
   // x_{m-2} and the output are the caller's rows only when m = 2
   if (!a.x_bf16 && !a.g_bf16 && !a.o_bf16)
-    hipLaunchKernelGGL((vjp_bwd_pair88_kernel<TB, F, F, F>), grid, dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL((vjp_bwd_pair_kernel<BA, BB, TB, F, F, F>), grid, dim3(kBwdThreads), 0, st, a);
   else if (!a.x_bf16 && a.g_bf16 && !a.o_bf16)
-    hipLaunchKernelGGL((vjp_bwd_pair88_kernel<TB, F, H16, F>), grid, dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL((vjp_bwd_pair_kernel<BA, BB, TB, F, H16, F>), grid, dim3(kBwdThreads), 0, st, a);
   else if (a.x_bf16 && a.g_bf16 && a.o_bf16)
-    hipLaunchKernelGGL((vjp_bwd_pair88_kernel<TB, H16, H16, H16>), grid, dim3(kBwdThreads), 0, st, a);
+    hipLaunchKernelGGL((vjp_bwd_pair_kernel<BA, BB, TB, H16, H16, H16>), grid, dim3(kBwdThreads), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <typename TB>
+hipError_t launch_pair(const VjpArgs& a, hipStream_t st) {
+  if (a.st.b == 8 && a.st2.b == 8) return launch_pair_ab<8, 8, TB>(a, st);
+  if (a.st.b == 5 && a.st2.b == 2) return launch_pair_ab<5, 2, TB>(a, st);
+  if (a.st.b == 3 && a.st2.b == 3) return launch_pair_ab<3, 3, TB>(a, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pair_any(DT bdt, const VjpArgs& a, hipStream_t st) {
@@ -603,9 +633,9 @@ hipError_t launch_apply_vjp(const Plan& pl, const void* blocks, DT bdt, const fl
   base.n_blk = pl.n_blk;
   base.partial = part;
 
-  // last two stages radix 8: one fused backward launch, which recomputes
-  // x_{m-1} itself
-  const bool pair = pl.m >= 2 && pl.radix[pl.m - 1] == 8 && pl.radix[pl.m - 2] == 8;
+  // last two stages of a compiled-in pair: one fused backward launch, which
+  // recomputes x_{m-1} itself
+  const bool pair = pl.m >= 2 && pair_compiled(pl.radix[pl.m - 2], pl.radix[pl.m - 1]);
   // forward: x_{t+1} = S_t x_t for t = 0 .. m-2 (m-3 with the fused pair)
   for (int t = 0; t + 1 < pl.m - (pair ? 1 : 0); ++t) {
     VjpArgs a = base;

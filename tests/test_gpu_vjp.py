@@ -184,13 +184,17 @@ def test_vjp_strided_rows(sch, d, io, pad):
         assert bool((base.float() == 7.0).all()), "dx written outside its rows"
 
 
-@pytest.mark.parametrize("sch,d", [((8, 8), 64), ((3, 8, 8), 192), ((2, 2, 8, 8), 256)])
+@pytest.mark.parametrize("sch,d", [((8, 8), 64), ((3, 8, 8), 192), ((2, 2, 8, 8), 256), ((5, 2), 10),
+                                   ((3, 5, 2), 30), ((7, 5, 2), 70), ((3, 3), 9), ((2, 3, 3), 18),
+                                   ((8, 8, 3, 3), 576)])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("blk", ["f32", "i8"])
 def test_vjp_fused_last_pair(sch, d, io, blk):
-    """Schedules ending in two radix-8 stages take the fused backward launch
-    for that pair (with m = 2 it reads x and writes dx itself, signs on both
-    sides); row counts that leave partial row groups and empty chunks."""
+    """Schedules ending in a compiled-in pair of stages ((8, 8), (5, 2),
+    (3, 3)) take the fused backward launch for that pair (with m = 2 it reads
+    x and writes dx itself, signs on both sides); units that leave lanes of a
+    wave idle, sets of units past the last one, and row counts that leave
+    partial row groups and empty chunks."""
     print(f"\n[case] vjp fused pair {sch} io={io} blk={blk}", flush=True)
     g_sign, g_theta, g_gauss, g_data = I.streams(I.BASE_SEED + 400 + d)
     theta = I.theta_params(g_theta, sch, d, 0.05, 0.1)
