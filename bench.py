@@ -328,11 +328,21 @@ def vjp_main(args) -> int:
     rd = rows * d
     # fp32 block-gradient partial sums in the workspace: one slot per backward workgroup
     nslot = (ws.numel() - 4 * rd * ((m - 1) + (2 if m > 1 else 0))) // (4 * nblk)
-    fwd = rd * (eb + 4) + (m - 2) * rd * 8 if m > 1 else 0
-    if m > 1:
-        bwd = rd * (eb + 4 + 4) + (m - 2) * rd * 12 + rd * (4 + eb + eb)
-    else:
+    # the library fuses the last two stages into one backward launch for
+    # these endings (and the forward then stops one stage earlier)
+    pair = m >= 2 and (sch[-2], sch[-1]) in ((8, 8), (5, 2), (3, 3))
+    nf = m - 2 if pair else m - 1                     # forward launches
+    fwd = (rd * (eb + 4) + (nf - 1) * rd * 8) if nf > 0 else 0
+    if m == 1:
         bwd = rd * 3 * eb
+    elif pair and m == 2:
+        bwd = rd * 3 * eb                             # x, dy -> dx
+    else:
+        # last launch(es): the pair reads x_{m-2} and dy, writes g_{m-2}; a
+        # single last stage reads x_{m-1} and dy, writes g_{m-1}
+        bwd = rd * (4 + eb + 4)
+        mid = (m - 3) if pair else (m - 2)            # fp32 stage launches in between
+        bwd += mid * rd * 12 + rd * (4 + eb + eb)     # ... and the first stage (x, dx in the I/O type)
     red = nslot * nblk * 4 * 2 + nblk * 4
     moved = fwd + bwd + red
     # dx = M^T dy is the inverse transform of dy for orthogonal blocks: the
