@@ -456,6 +456,14 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   if constexpr (N + 1 < RT) pipe_round<Sch, N + 1, TR, DOUT, T, TB>(p, tile, cf, xv, gA, gB, rot, j, row0, nr);
 }
 
+// bf16 rows copied out through LDS (not stored by the last stage): the
+// compute waves, idle until the next tile is in, copy out one micro-block per
+// thread and the data waves the other half, then the data waves write the
+// prefetched tile (fp32 rows keep the data-wave swap: a whole prefetched
+// fp32 tile does not fit the data waves' registers).
+template <typename T, bool DOUT>
+constexpr bool kPSharedOut = !DOUT && std::is_same<T, uint16_t>::value;
+
 template <class Sch, bool TR, bool DOUT, typename T, typename TB>
 __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
   constexpr int RT = rounds_before_rt<Sch>(Sch::M);
@@ -466,9 +474,12 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
   if (tix >= p.ntiles) return;   // uniform per workgroup
   if (threadIdx.x >= 64 * kPCW) {
     // 2 x 512 (bf16) or 2 x 1024 (fp32) micro-blocks over 256 data threads
-    constexpr bool F = std::is_same<T, float>::value;
-    data_waves_exact<T, typename Sch::Lay, 64 * kPIOW, F ? 8 : 4, 4, 2, DOUT, false>(p, tile,
+    if constexpr (kPSharedOut<T, DOUT>)
+      data_waves_shared_out<T, typename Sch::Lay, 64 * kPIOW, 4, 2, 64 * kPCW, false>(p, tile,
                                                                                    threadIdx.x - 64 * kPCW);
+    else
+      data_waves_exact<T, typename Sch::Lay, 64 * kPIOW, std::is_same<T, float>::value ? 8 : 4, 4, 2, DOUT, false>(
+          p, tile, threadIdx.x - 64 * kPCW);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -498,6 +509,7 @@ __global__ void __launch_bounds__(kPThreads) apply_pipe_kernel(RowParams p) {
     const int nr = tile_rows(p, tix);
     read_inputs<Sch, S0::B, S0::S>(tile, grp_round<S0::S>(rot % R0) + lane_grp<S0::S>(gA, gB), j, xv[0]);
     pipe_round<Sch, 0, TR, DOUT, T, TB>(p, tile, cf, xv, gA, gB, rot, j, row0, nr);
+    if constexpr (kPSharedOut<T, DOUT>) compute_copy_out<T, typename Sch::Lay, 64 * kPCW, 1>(p, tile, tix, threadIdx.x);
     __syncthreads();   // data waves have swapped the tile
   }
 }
@@ -716,9 +728,14 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
   int64_t tix = blockIdx.x;
   if (tix >= p.ntiles) return;   // uniform per workgroup
   if (threadIdx.x >= 64 * k5CW) {
-    // 2 x 640 (bf16) or 2 x 1280 (fp32) micro-blocks over 256 data threads
-    constexpr bool F = std::is_same<T, float>::value;
-    data_waves_exact<T, Lay, 64 * k5IOW, F ? 10 : 5, F ? 4 : 5, 4, false, true>(p, tile, threadIdx.x - 64 * k5CW);
+    // 2 x 640 (bf16) or 2 x 1280 (fp32) micro-blocks over 256 data threads;
+    // for bf16 rows the compute waves store two micro-blocks per thread of
+    // the finished tile and the data waves the rest (fp32 rows: the data
+    // waves swap alone, the prefetched fp32 tile does not fit their registers)
+    if constexpr (std::is_same<T, float>::value)
+      data_waves_exact<T, Lay, 64 * k5IOW, 10, 4, 4, false, true>(p, tile, threadIdx.x - 64 * k5CW);
+    else
+      data_waves_shared_out<T, Lay, 64 * k5IOW, 5, 4, 2 * 64 * k5CW, true>(p, tile, threadIdx.x - 64 * k5CW);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -756,6 +773,7 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
       stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
+    if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
     __syncthreads();   // data waves have swapped the tile
     tix += gridDim.x;
     if (tix >= p.ntiles) break;
@@ -779,6 +797,7 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
       stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
+    if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
     __syncthreads();   // data waves have swapped the tile
     tix += gridDim.x;
     if (tix >= p.ntiles) break;

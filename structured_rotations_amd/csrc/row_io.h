@@ -333,6 +333,108 @@ __device__ __forceinline__ void data_waves_exact(const RowParams& p, float* tile
   }
 }
 
+// Stores micro-block `blk` (row quad blk / chunks, chunk blk % chunks) of the
+// finished tile to y, the inverse's row signs applied on the way.  Rows past a
+// ragged tile are clamped to its last row (the same values to the same
+// address).
+template <typename T, class Lay>
+__device__ __forceinline__ void io_copy_out(const RowParams& p, const float* tile, int64_t row0, int nr, int blk) {
+  constexpr int V = Io<T>::V;
+  const int q = blk >= p.chunks ? 1 : 0;
+  const int c = blk - q * p.chunks;
+  uint2 osg = uint2{0u, 0u};
+  if (p.sign_mode == 2) {
+    const int8_t* sp = p.signs + c * V;
+    if constexpr (V == 8) osg = *reinterpret_cast<const uint2*>(sp);
+    else osg.x = *reinterpret_cast<const uint32_t*>(sp);
+  }
+  T* y = static_cast<T*>(p.y);
+  const float* plane = tile + q * 4 * Lay::units(p.d);
+  f32x4 col[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) col[e] = *reinterpret_cast<const f32x4*>(plane + 4 * Lay::unit(c * V + e));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const uint32_t neg = (((e < 4 ? osg.x : osg.y) >> (8 * (e & 3))) & 0x80u) << 24;
+      v[e] = sgnf(col[e][i], neg);
+    }
+    const int r = 4 * q + i < nr ? 4 * q + i : nr - 1;
+    st_stream(y + (row0 + r) * p.ldy + (int64_t)c * V, pack_row<T>(v));
+  }
+}
+
+// The compute waves' part of a shared copy-out (see data_waves_shared_out):
+// compute thread t stores micro-blocks t + k * NCT, k < KC, then the barrier
+// after which the data waves overwrite the tile.
+template <typename T, class Lay, int NCT, int KC>
+__device__ __forceinline__ void compute_copy_out(const RowParams& p, const float* tile, int64_t tix, int t) {
+  const int nr = tile_rows(p, tix);
+#pragma unroll
+  for (int k = 0; k < KC; ++k) io_copy_out<T, Lay>(p, tile, tix * kRows, nr, t + k * NCT);
+  __syncthreads();
+}
+
+// Data waves that share the copy-out of the finished tile with the compute
+// waves, which would otherwise wait at the swap barrier: every slot of the
+// next tile is prefetched into registers over the NB stage barriers (NS slots
+// per thread, 2 * chunks == NS * kIoT); after the last stage the compute
+// threads store micro-blocks 0 .. CB-1 (compute_copy_out) and data thread it
+// stores CB + it + k * kIoT; one barrier, then the prefetched tile goes into
+// LDS and one more barrier releases the compute waves.  Barriers per tile:
+// NB + 2, after one initial barrier.  SPREAD: slot u of the prefetch goes out
+// after barrier u * NB / NS (spread over the stages), else all at the tile start.
+template <typename T, class Lay, int kIoT, int NS, int NB, int CB, bool SPREAD>
+__device__ __forceinline__ void data_waves_shared_out(const RowParams& p, float* tile, int it) {
+  static_assert(CB % kIoT == 0 && CB <= NS * kIoT, "the data threads' share is whole rounds of micro-blocks");
+  constexpr int ND = (NS * kIoT - CB) / kIoT;
+  int64_t tix = blockIdx.x;
+  int qs[NS], cs[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int i = it + u * kIoT;
+    qs[u] = i >= p.chunks ? 1 : 0;
+    cs[u] = i - qs[u] * p.chunks;
+  }
+  {
+    const int nr = tile_rows(p, tix);
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      IoBlock one;
+      io_load<T>(p, tix * kRows, nr, qs[u], cs[u], one);
+      io_to_lds<T, Lay>(p, tile, qs[u], cs[u], one);
+    }
+  }
+  __syncthreads();
+  IoBlock pf[NS];
+  for (; tix < p.ntiles; tix += gridDim.x) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) asm volatile("" : "+v"(qs[u]), "+v"(cs[u]));
+    const int64_t row0 = tix * kRows;
+    const int nr = tile_rows(p, tix);
+    const int64_t nxt = tix + gridDim.x;
+    const bool has_next = nxt < p.ntiles;
+    const int nr_next = has_next ? tile_rows(p, nxt) : 1;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if ((SPREAD ? u * NB / NS : 0) == b && has_next) io_load<T>(p, nxt * kRows, nr_next, qs[u], cs[u], pf[u]);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < ND; ++k) io_copy_out<T, Lay>(p, tile, row0, nr, CB + it + k * kIoT);
+    __syncthreads();
+    if (has_next) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) io_to_lds<T, Lay>(p, tile, qs[u], cs[u], pf[u]);
+    }
+    __syncthreads();
+  }
+}
+
 // Host side: kernel parameters for rows of length pl.d (stages in processing
 // order, reversed for the inverse).
 inline RowParams make_row_params(const Plan& pl, bool inverse, const void* blocks, const float* scales,
