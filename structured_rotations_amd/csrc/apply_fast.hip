@@ -684,22 +684,45 @@ constexpr int k5Threads = 64 * (k5CW + k5IOW);
 
 // One radix-8 stage of the 5120 kernel (5 rounds, stride S, stage params sd),
 // coefficient buffers alternating; on exit the next stage's first round is in
-// the buffer given by the round parity.
+// the buffer given by the round parity.  Forward rounds read the next
+// round's inputs while their own h = 1 chain runs (products_write); the
+// inverse keeps one round's inputs at a time (its element-wise coefficient
+// loads leave no registers for a second set).
 template <class Lay, int S, bool TR, typename TB, typename NextLoad>
 __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, const StageFast& sd, Cbuf& X, Cbuf& Y,
                                             int gb, int j, NextLoad next) {
   using Sch = Sched<5120, Lay, List<St<8, S>>>;
   // rounds 0..4: X holds round 0
-  load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
-  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 0 * kGPR + gb, as8(X), 0, 0, j);
-  load_coef<8, TB, TR>(p, sd, 2 * kGPR, gb, j, as8(X));
-  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 1 * kGPR + gb, as8(Y), 0, 0, j);
-  load_coef<8, TB, TR>(p, sd, 3 * kGPR, gb, j, as8(Y));
-  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 2 * kGPR + gb, as8(X), 0, 0, j);
-  load_coef<8, TB, TR>(p, sd, 4 * kGPR, gb, j, as8(X));
-  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 3 * kGPR + gb, as8(Y), 0, 0, j);
-  next(Y);   // the next stage's round 0 goes to Y
-  round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 4 * kGPR + gb, as8(X), 0, 0, j);
+  if constexpr (!TR) {
+    float xa[2][8], xb[2][8];
+    read_inputs<Sch, 8, S>(tile, 0 * kGPR + gb, j, xa);
+    load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 0 * kGPR + gb, 1 * kGPR + gb, as8(X), xa, xb,
+                                                             0, 0, j);
+    load_coef<8, TB, TR>(p, sd, 2 * kGPR, gb, j, as8(X));
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 1 * kGPR + gb, 2 * kGPR + gb, as8(Y), xb, xa,
+                                                             0, 0, j);
+    load_coef<8, TB, TR>(p, sd, 3 * kGPR, gb, j, as8(Y));
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 2 * kGPR + gb, 3 * kGPR + gb, as8(X), xa, xb,
+                                                             0, 0, j);
+    load_coef<8, TB, TR>(p, sd, 4 * kGPR, gb, j, as8(X));
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 3 * kGPR + gb, 4 * kGPR + gb, as8(Y), xb, xa,
+                                                             0, 0, j);
+    next(Y);   // the next stage's round 0 goes to Y
+    products_write<Sch, 8, S, false, false, uint16_t, TB, TR>(p, tile, 4 * kGPR + gb, 4 * kGPR + gb, as8(X), xa, xb,
+                                                              0, 0, j);
+  } else {
+    load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
+    round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 0 * kGPR + gb, as8(X), 0, 0, j);
+    load_coef<8, TB, TR>(p, sd, 2 * kGPR, gb, j, as8(X));
+    round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 1 * kGPR + gb, as8(Y), 0, 0, j);
+    load_coef<8, TB, TR>(p, sd, 3 * kGPR, gb, j, as8(Y));
+    round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 2 * kGPR + gb, as8(X), 0, 0, j);
+    load_coef<8, TB, TR>(p, sd, 4 * kGPR, gb, j, as8(X));
+    round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 3 * kGPR + gb, as8(Y), 0, 0, j);
+    next(Y);   // the next stage's round 0 goes to Y
+    round_compute<Sch, 8, S, TR, false, uint16_t, TB>(p, tile, 4 * kGPR + gb, as8(X), 0, 0, j);
+  }
   __syncthreads();
 }
 
