@@ -573,6 +573,10 @@ __device__ __forceinline__ float ld_scale(const RowParams& p, int grp) {
 // stage, s2: the radix-2 stage.  Forward: c5[d4][h][k] = C5_{2g+d4}[o][k],
 // o = min(4h + j, 4), and the two 2 x 2 blocks of columns o (h = 0, 1).
 // Inverse: c5[d4][h][k] = C5_{2g+d4}[k][o] and all five 2 x 2 blocks.
+// Forward bf16 and int8 coefficients stay as loaded (raw bits in the slots,
+// int8 group scales in slots 28..31) and decode_tail widens them where the
+// round uses them, so the load's wait does not land where it is issued; the
+// inverse widens at load (its slots are all taken).
 template <typename TB, bool TR>
 __device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s5, const StageFast& s2, int g0,
                                           int gb, int j, Cbuf& c) {
@@ -594,6 +598,15 @@ __device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s
         const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + o * 5) * 4, soff5, 0);
         d[0] = __uint_as_float(a.x); d[1] = __uint_as_float(a.y); d[2] = __uint_as_float(a.z); d[3] = __uint_as_float(a.w);
         d[4] = ld_coef1<TB>(rs, base + o * 5 + 4, soff5, sc);
+      } else if constexpr (!TR && std::is_same<TB, uint16_t>::value) {
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+          d[k] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (base + o * 5 + k) * 2, soff5, 0));
+      } else if constexpr (!TR) {
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+          d[k] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, base + o * 5 + k, soff5, 0));
+        if (h == 0) c.v[28 + d4] = sc;
       } else {
 #pragma unroll
         for (int k = 0; k < 5; ++k) d[k] = ld_coef1<TB>(rs, base + (TR ? k * 5 + o : o * 5 + k), soff5, sc);
@@ -603,7 +616,17 @@ __device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int o = 4 * h + j < 5 ? 4 * h + j : 4;
-      ld_coef4<TB>(rs, (5 * gb + o) * 4, soff2, ld_scale<TB>(p, s2.grp_off + 5 * (g0 + gb) + o), &c.v[20 + 4 * h]);
+      const int voff = (5 * gb + o) * 4 * SZ;
+      if constexpr (std::is_same<TB, float>::value) {
+        ld_coef4<TB>(rs, (5 * gb + o) * 4, soff2, 1.0f, &c.v[20 + 4 * h]);
+      } else if constexpr (std::is_same<TB, uint16_t>::value) {
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff2, 0);
+        c.v[20 + 4 * h] = __uint_as_float(a.x);
+        c.v[21 + 4 * h] = __uint_as_float(a.y);
+      } else {
+        c.v[20 + 4 * h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff2, 0));
+        c.v[30 + h] = ld_scale<TB>(p, s2.grp_off + 5 * (g0 + gb) + o);
+      }
     }
   } else {
 #pragma unroll
@@ -612,8 +635,37 @@ __device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s
   }
 }
 
-template <class Lay, bool TR>
-__device__ __forceinline__ void tail_round(float* tile, int g, const Cbuf& c, int j) {
+// The fp32 tail coefficients of a buffer filled by load_tail.
+template <typename TB, bool TR>
+__device__ __forceinline__ void decode_tail(const Cbuf& raw, Cbuf& c) {
+  if constexpr (TR || std::is_same<TB, float>::value) {
+#pragma unroll
+    for (int i = 0; i < 40; ++i) c.v[i] = raw.v[i];
+  } else if constexpr (std::is_same<TB, uint16_t>::value) {
+#pragma unroll
+    for (int i = 0; i < 20; ++i) c.v[i] = __uint_as_float(__float_as_uint(raw.v[i]) << 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t a = __float_as_uint(raw.v[20 + 4 * h]), b = __float_as_uint(raw.v[21 + 4 * h]);
+      c.v[20 + 4 * h] = bf16_lo(a); c.v[21 + 4 * h] = bf16_hi(a);
+      c.v[22 + 4 * h] = bf16_lo(b); c.v[23 + 4 * h] = bf16_hi(b);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 20; ++i) c.v[i] = (float)(int8_t)__float_as_uint(raw.v[i]) * raw.v[28 + i / 10];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t a = __float_as_uint(raw.v[20 + 4 * h]);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) c.v[20 + 4 * h + n] = (float)(int8_t)(a >> (8 * n)) * raw.v[30 + h];
+    }
+  }
+}
+
+template <class Lay, bool TR, typename TB>
+__device__ __forceinline__ void tail_round(float* tile, int g, const Cbuf& craw, int j) {
+  Cbuf c;
+  decode_tail<TB, TR>(craw, c);
   constexpr int PLANE = 4 * Lay::units(5120);
   const int col0 = 10 * g;
   float x[2][2][5];   // [q][d4][d3]: row 4q + j, column col0 + 2 d3 + d4
@@ -732,13 +784,13 @@ __device__ __forceinline__ void stage_tail_5120(const RowParams& p, float* tile,
                                                 NextLoad next) {
   // rounds 0..3: X holds round 0
   load_tail<TB, TR>(p, s5, s2, 1 * kGPR, gb, j, Y);
-  tail_round<Lay, TR>(tile, 0 * kGPR + gb, X, j);
+  tail_round<Lay, TR, TB>(tile, 0 * kGPR + gb, X, j);
   load_tail<TB, TR>(p, s5, s2, 2 * kGPR, gb, j, X);
-  tail_round<Lay, TR>(tile, 1 * kGPR + gb, Y, j);
+  tail_round<Lay, TR, TB>(tile, 1 * kGPR + gb, Y, j);
   load_tail<TB, TR>(p, s5, s2, 3 * kGPR, gb, j, Y);
-  tail_round<Lay, TR>(tile, 2 * kGPR + gb, X, j);
+  tail_round<Lay, TR, TB>(tile, 2 * kGPR + gb, X, j);
   next(X);   // the next stage's round 0 goes to X
-  tail_round<Lay, TR>(tile, 3 * kGPR + gb, Y, j);
+  tail_round<Lay, TR, TB>(tile, 3 * kGPR + gb, Y, j);
   __syncthreads();
 }
 
