@@ -382,8 +382,9 @@ __device__ __forceinline__ void compute_copy_out(const RowParams& p, const float
 // next tile is prefetched into registers over the NB stage barriers (NS slots
 // per thread, 2 * chunks == NS * kIoT); after the last stage the compute
 // threads store micro-blocks 0 .. CB-1 (compute_copy_out) and data thread it
-// stores CB + it + k * kIoT; one barrier, then the prefetched tile goes into
-// LDS and one more barrier releases the compute waves.  Barriers per tile:
+// stores CB + it + k * kIoT, refilling each at once; one barrier, then the
+// rest of the prefetched tile goes into LDS and one more barrier releases
+// the compute waves.  Barriers per tile:
 // NB + 2, after one initial barrier.  SPREAD: slot u of the prefetch goes out
 // after barrier u * NB / NS (spread over the stages), else all at the tile start.
 template <typename T, class Lay, int kIoT, int NS, int NB, int CB, bool SPREAD>
@@ -424,12 +425,19 @@ __device__ __forceinline__ void data_waves_shared_out(const RowParams& p, float*
         if ((SPREAD ? u * NB / NS : 0) == b && has_next) io_load<T>(p, nxt * kRows, nr_next, qs[u], cs[u], pf[u]);
       __syncthreads();
     }
+    // the data thread's own micro-blocks are its slots U0 .. NS-1: each is
+    // refilled right after it is stored, the compute waves' ones after the
+    // barrier that ends their copy-out
+    constexpr int U0 = CB / kIoT;
 #pragma unroll
-    for (int k = 0; k < ND; ++k) io_copy_out<T, Lay>(p, tile, row0, nr, CB + it + k * kIoT);
+    for (int k = 0; k < ND; ++k) {
+      io_copy_out<T, Lay>(p, tile, row0, nr, CB + it + k * kIoT);
+      if (has_next) io_to_lds<T, Lay>(p, tile, qs[U0 + k], cs[U0 + k], pf[U0 + k]);
+    }
     __syncthreads();
     if (has_next) {
 #pragma unroll
-      for (int u = 0; u < NS; ++u) io_to_lds<T, Lay>(p, tile, qs[u], cs[u], pf[u]);
+      for (int u = 0; u < U0; ++u) io_to_lds<T, Lay>(p, tile, qs[u], cs[u], pf[u]);
     }
     __syncthreads();
   }
