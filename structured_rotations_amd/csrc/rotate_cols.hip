@@ -93,11 +93,12 @@ __device__ __forceinline__ ColTile col_tile(const ColParams& p, int64_t tix) {
 // Coefficients of one stage of one tile, C[o][k] (C = B forward, B^T
 // inverse), fetched into registers a stage ahead as the stored words (fp32
 // bits, bf16 bits, or int8 code and its fp32 scale); coef_put turns them into
-// fp32.  Thread t fetches elements e = t + u * 512 of the ngl * b * b, NCU of
-// them; slots past the stage's count repeat its last element.  Every thread
-// issues exactly NCU loads (2 NCU for int8) and nothing is computed from them
-// before coef_put, so the wait in front of coef_put is for these loads and the
-// ones before them, never for the tile prefetch issued after them.
+// fp32.  Thread t fetches elements e = t + u * 512 of the ngl * b * b for
+// u < ncu = ceil(ngl * b * b / 512) (at most NCU); slots past the stage's
+// count repeat its last element.  Every thread issues the same ncu loads (2 ncu
+// for int8) and nothing is computed from them before coef_put, so the wait in
+// front of coef_put is for these loads and the ones before them, never for the
+// tile prefetch issued after them.
 template <typename TB, int NCU>
 __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColTile& t, uint32_t (&cw)[NCU],
                                            float (&csc)[NCU]) {
@@ -111,6 +112,7 @@ __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColT
   const int sufi = (int)p.suf;
 #pragma unroll
   for (int u = 0; u < NCU; ++u) {
+    if (u >= cs.ncu) break;   // uniform: slots past the stage's count are never put
     int e = threadIdx.x + u * 512;
     e = e < n ? e : n - 1;
     const int gl = udiv(e, cs.mag_bb);
@@ -126,7 +128,8 @@ __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColT
       cw[u] = (uint32_t)(int)*src;
       csc[u] = scales[gl * sufi];
     }
-  }}
+  }
+}
 
 // Writes the fetched coefficients into a slot as C[gl][o][k] in fp32 with
 // rows padded to 4 floats (the layout the stage tasks read).
