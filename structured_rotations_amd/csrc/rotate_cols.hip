@@ -26,6 +26,9 @@ struct ColStage {
   uint32_t mag_b, mag_bb;   // ceil(2^32 / b), ceil(2^32 / b^2) (see udiv)
   uint32_t mag_ls;          // same for ls (0 for ls = 1)
   int ncu;                  // coefficient slots per thread: ceil(nsub * b / 512)
+  int nq;                   // quad path (b even, blk_off a multiple of 4; the kernels that
+                            // compile it in): 4-element quads per thread,
+                            // ceil(nsub * b / 2048); 0 for the one-element path
 };
 
 struct ColParams {
@@ -99,7 +102,7 @@ __device__ __forceinline__ ColTile col_tile(const ColParams& p, int64_t tix) {
 // for int8) and nothing is computed from them before coef_put, so the wait in
 // front of coef_put is for these loads and the ones before them, never for the
 // tile prefetch issued after them.
-template <typename TB, int NCU>
+template <typename TB, int NCU, bool QUAD>
 __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColTile& t, uint32_t (&cw)[NCU],
                                            float (&csc)[NCU]) {
   const ColStage& cs = p.st[s];
@@ -110,6 +113,34 @@ __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColT
                      (t.pre * (int64_t)ngl * p.suf + t.q) * BB;
   const float* scales = p.scales + cs.grp_off + t.pre * (int64_t)ngl * p.suf + t.q;
   const int sufi = (int)p.suf;
+  if (QUAD && cs.nq > 0) {
+    // quads of 4 consecutive stored elements (never across a block: b^2 is a
+    // multiple of 4), one 16-, 8- or 4-byte load each, in memory order
+#pragma unroll
+    for (int v = 0; v < NCU / 4; ++v) {
+      if (v >= cs.nq) break;   // uniform
+      int e = 4 * ((int)threadIdx.x + v * 512);
+      e = e < n ? e : n - 4;
+      const int gl = udiv(e, cs.mag_bb);
+      const TB* src = blocks + gl * sufi * BB + (e - gl * BB);
+      if constexpr (std::is_same<TB, float>::value) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(src);
+        cw[4 * v] = a.x; cw[4 * v + 1] = a.y; cw[4 * v + 2] = a.z; cw[4 * v + 3] = a.w;
+      } else if constexpr (std::is_same<TB, uint16_t>::value) {
+        const uint2 a = *reinterpret_cast<const uint2*>(src);
+        cw[4 * v] = a.x & 0xffffu; cw[4 * v + 1] = a.x >> 16; cw[4 * v + 2] = a.y & 0xffffu; cw[4 * v + 3] = a.y >> 16;
+      } else {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(src);
+        const float sc = scales[gl * sufi];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          cw[4 * v + c] = (uint32_t)(int)(int8_t)(a >> (8 * c));
+          csc[4 * v + c] = sc;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < NCU; ++u) {
     if (u >= cs.ncu) break;   // uniform: slots past the stage's count are never put
@@ -133,12 +164,36 @@ __device__ __forceinline__ void coef_fetch(const ColParams& p, int s, const ColT
 
 // Writes the fetched coefficients into a slot as C[gl][o][k] in fp32 with
 // rows padded to 4 floats (the layout the stage tasks read).
-template <typename TB, int NCU>
+template <typename TB, int NCU, bool QUAD>
 __device__ __forceinline__ void coef_put(const ColParams& p, int s, const uint32_t (&cw)[NCU], const float (&csc)[NCU],
                                          float* slot) {
   const ColStage& cs = p.st[s];
   const int B = cs.b, BB = B * B, Bp = (B + 3) & ~3;
   const int n = (p.nsub / B) * BB;
+  auto decode = [&](int u) {
+    if constexpr (std::is_same<TB, float>::value) return __uint_as_float(cw[u]);
+    else if constexpr (std::is_same<TB, uint16_t>::value) return __uint_as_float(cw[u] << 16);
+    else return (float)(int)cw[u] * csc[u];
+  };
+  if (QUAD && cs.nq > 0) {
+    // stored element m of block gl is C[m / B][m % B] forward, C[m % B][m / B]
+    // transposed
+#pragma unroll
+    for (int v = 0; v < NCU / 4; ++v) {
+      const int e = 4 * ((int)threadIdx.x + v * 512);
+      if (v < cs.nq && e < n) {
+        const int gl = udiv(e, cs.mag_bb);
+        const int m0 = e - gl * BB;
+        float* g = slot + gl * (B * Bp);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int hi = udiv(m0 + c, cs.mag_b), lo = m0 + c - hi * B;
+          g[p.transpose ? lo * Bp + hi : hi * Bp + lo] = decode(4 * v + c);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < NCU; ++u) {
     const int e = threadIdx.x + u * 512;
@@ -146,11 +201,7 @@ __device__ __forceinline__ void coef_put(const ColParams& p, int s, const uint32
       const int gl = udiv(e, cs.mag_bb);
       const int i = e - gl * BB;
       const int o = udiv(i, cs.mag_b);
-      float v;
-      if constexpr (std::is_same<TB, float>::value) v = __uint_as_float(cw[u]);
-      else if constexpr (std::is_same<TB, uint16_t>::value) v = __uint_as_float(cw[u] << 16);
-      else v = (float)(int)cw[u] * csc[u];
-      slot[gl * (B * Bp) + o * Bp + (i - o * B)] = v;
+      slot[gl * (B * Bp) + o * Bp + (i - o * B)] = decode(u);
     }
   }
 }
@@ -471,6 +522,11 @@ __device__ __forceinline__ void col_swap_el(const ColParams& p, const ColTile& d
 template <typename TIN, typename TOUT, typename TB, bool BIG, bool VEC, int MAXC>
 __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   constexpr int NCU = BIG ? 16 : 8;
+  // the quad coefficient path is compiled into the bf16-input kernels of more
+  // than 4 chunks per thread: the 4-chunk ones must stay at 128 VGPRs (two
+  // workgroups per CU), and in the fp32-input ones the second path slowed the
+  // one-element path of the radix-3 pass by 15%
+  constexpr bool kQuad = MAXC > 4 && std::is_same<TIN, uint16_t>::value;
   extern __shared__ float tile[];
   float* slots = tile + p.nsub * p.pw;
   const int lane = threadIdx.x & 63;
@@ -483,8 +539,8 @@ __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   uint32_t cw[NCU];
   float csc[NCU];
   // prologue: first tile and its first stage's coefficients in place
-  coef_fetch<TB, NCU>(p, 0, t, cw, csc);
-  coef_put<TB, NCU>(p, 0, cw, csc, slots);
+  coef_fetch<TB, NCU, kQuad>(p, 0, t, cw, csc);
+  coef_put<TB, NCU, kQuad>(p, 0, cw, csc, slots);
   u32x4 pf[MAXC];
   uint8_t pfs[MAXC];
   uint32_t smask = 0;
@@ -498,7 +554,7 @@ __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
   int sn = 1;
   int64_t tixn = tix;
   if (sn == p.nstage) { sn = 0; tixn = tix + gridDim.x; }
-  coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cw, csc);
+  coef_fetch<TB, NCU, kQuad>(p, sn, col_tile(p, clampt(tixn)), cw, csc);
   __syncthreads();
   int slot = 0;
   while (true) {
@@ -506,10 +562,10 @@ __global__ void __launch_bounds__(512) col_pass_kernel(ColParams p) {
       // coefficients of the next stage into the other slot, then fetch the
       // one after; the next tile's prefetch goes out behind the first
       // stage's fetch, so the first two stages never wait for it
-      if (tixn < p.ntiles) coef_put<TB, NCU>(p, sn, cw, csc, slots + (slot ^ 1) * p.cslot);
+      if (tixn < p.ntiles) coef_put<TB, NCU, kQuad>(p, sn, cw, csc, slots + (slot ^ 1) * p.cslot);
       ++sn;
       if (sn == p.nstage) { sn = 0; tixn += gridDim.x; }
-      coef_fetch<TB, NCU>(p, sn, col_tile(p, clampt(tixn)), cw, csc);
+      coef_fetch<TB, NCU, kQuad>(p, sn, col_tile(p, clampt(tixn)), cw, csc);
       if constexpr (VEC) {
         if (s == 0) col_prefetch<TIN, MAXC>(p, col_tile(p, clampt(tix + gridDim.x)), pf, pfs);
       }
@@ -606,6 +662,7 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
     cs.mag_bb = mag(cs.b * cs.b);
     cs.mag_ls = mag(cs.ls);
     cs.ncu = (nsub * cs.b + 511) / 512;
+    cs.nq = (cs.b % 2 == 0 && cs.blk_off % 4 == 0) ? (nsub * cs.b + 2047) / 2048 : 0;
     bmax = cs.b > bmax ? cs.b : bmax;
     cw = ((cs.b + 3) & ~3) > cw ? ((cs.b + 3) & ~3) : cw;
   }
@@ -613,9 +670,6 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
   // at most 8 (radix <= 8) or 16 per thread.
   const bool big = bmax > 8;
   if ((size_t)nsub * bmax > (size_t)512 * (big ? 16 : 8)) return hipErrorInvalidValue;
-  // Panel width: the widest multiple of 64 columns (at most 512) whose fp32
-  // tile plus two coefficient slots fit in 160 KiB (stage tasks are 64-column
-  // blocks).
   p.cslot = nsub * cw;
   // Panel width: a multiple of 64 columns (stage tasks are 64-column blocks)
   // up to 1024, as wide as fits next to two coefficient slots in 80 KiB (two
