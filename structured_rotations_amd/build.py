@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libharp.so")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-HIP_SOURCES = ["api.hip", "apply_tile.hip", "apply_mfma.hip", "apply_valu.hip", "apply_fast.hip", "rht.hip", "rotate_cols.hip", "materialize.hip", "decode.hip", "vjp.hip"]
+HIP_SOURCES = ["api.hip", "apply_tile.hip", "apply_mfma.hip", "apply_valu.hip", "apply_fast.hip", "rht.hip", "rotate_cols.hip", "col_dense.hip", "materialize.hip", "decode.hip", "vjp.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 DEVICE_FLAGS = [
@@ -42,7 +42,7 @@ KERNEL_SOURCES = {
     "apply_pipe": ["apply_fast.hip", "row_io.h", "common.h"],
     "apply_5120": ["apply_fast.hip", "row_io.h", "common.h"],
     "rht_wave": ["rht.hip", "common.h"],
-    "col_pass": ["rotate_cols.hip", "apply_fast.hip", "row_io.h", "common.h", "api.hip"],
+    "col_pass": ["rotate_cols.hip", "col_dense.hip", "apply_fast.hip", "row_io.h", "common.h", "api.hip"],
 }
 
 

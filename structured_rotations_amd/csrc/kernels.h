@@ -50,6 +50,15 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
                              const void* x, int64_t ldx, DT in_dt, void* y, int64_t ldy,
                              DT out_dt, int64_t ncols, hipStream_t stream);
 
+// Column runs of at most 32 rows (the product of the radices of stages
+// [t0, t1)): one dense nsub x nsub product per row group on the matrix cores;
+// launch_apply_cols hands such runs over.  Any column count and row stride.
+bool cols_dense_supported(const Plan& pl, int t0, int t1);
+hipError_t launch_apply_cols_dense(const Plan& pl, int t0, int t1, bool inverse, const void* blocks, DT bdt,
+                                   const float* scales, const int8_t* signs, int sign_mode, const void* x,
+                                   int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt, int64_t ncols,
+                                   hipStream_t stream);
+
 // k composed randomized Hadamard transforms over rows (all radices powers of two).
 hipError_t launch_rht(const Plan& pl, const int8_t* signs, int k, bool inverse, const void* x,
                       int64_t ldx, DT in_dt, void* y, int64_t ldy, DT out_dt, int64_t rows,

@@ -641,6 +641,9 @@ hipError_t launch_apply_cols(const Plan& pl, int t0, int t1, bool inverse, const
                              const void* x, int64_t ldx, DT in_dt, void* y, int64_t ldy,
                              DT out_dt, int64_t ncols, hipStream_t stream) {
   if (ncols <= 0) return hipSuccess;
+  if (cols_dense_supported(pl, t0, t1))
+    return launch_apply_cols_dense(pl, t0, t1, inverse, blocks, bdt, scales, signs, sign_mode, x, ldx, in_dt, y, ldy,
+                                   out_dt, ncols, stream);
   ColParams p{};
   int nsub = 1;
   for (int t = t0; t < t1; ++t) nsub *= pl.radix[t];
