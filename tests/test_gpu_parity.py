@@ -413,6 +413,47 @@ def test_rotate_weight_block_types(blk, io):
     _rotate_round_trip(c, io, blk, None, f"two-sided {blk}/{io}")
 
 
+def _two_sided_case(seed, su, du, sv, dv, io):
+    rng = np.random.default_rng(seed)
+    c = {"su": su, "sv": sv, "du": du, "dv": dv}
+    c["tu"] = rng.standard_normal(sum(O.theta_counts(su, du))) * 0.05
+    c["tv"] = rng.standard_normal(sum(O.theta_counts(sv, dv))) * 0.05
+    c["gu"] = I.gauss_mats(rng, su)
+    c["gv"] = I.gauss_mats(rng, sv)
+    c["su_s"] = np.where(rng.integers(0, 2, du) == 1, 1, -1).astype(np.int8)
+    c["sv_s"] = np.where(rng.integers(0, 2, dv) == 1, 1, -1).astype(np.int8)
+    c["w"] = W.round_io((rng.standard_normal((du, dv)) * 0.02).astype(np.float32), io)
+    return c
+
+
+@pytest.mark.parametrize("sv,dv", [((8, 16), 128), ((3, 5), 15)])
+@pytest.mark.parametrize("blk", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_dense_column_run(sv, dv, blk, io):
+    # U (8, 8, 8, 3, 3) on 4608 rows: the second pass is a run of 9 rows,
+    # applied as one composed 9 x 9 product per row group (two columns per
+    # lane for bf16 input with an even column count, one otherwise), with
+    # every stored block type
+    print(f"\n[case] two-sided dense column run blk={blk} io={io} dv={dv}", flush=True)
+    c = _two_sided_case(47 + dv, (8, 8, 8, 3, 3), 4608, sv, dv, io)
+    _rotate_round_trip(c, io, blk, None, f"two-sided dense run {blk}/{io}/{dv}")
+
+
+@pytest.mark.parametrize("dv", [128, 15])
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_rotate_weight_dense_single_run(dv, use_ws, io):
+    # U (3, 3, 3) on 27 rows: the whole U side is one composed 27 x 27 product
+    # per column, so the row signs go in on its input (forward) and on its
+    # output (inverse)
+    print(f"\n[case] two-sided single dense run io={io} ws={use_ws} dv={dv}", flush=True)
+    sv = (8, 16) if dv == 128 else (3, 5)
+    c = _two_sided_case(53 + dv, (3, 3, 3), 27, sv, dv, io)
+    ws = torch.empty(api.harp_rotate_weight_workspace(27, dv) // 4, dtype=torch.float32,
+                     device="cuda") if use_ws else None
+    _rotate_round_trip(c, io, "f32", ws, f"two-sided single dense run {io}/{use_ws}/{dv}")
+
+
 @pytest.mark.parametrize("su,du", [((8, 8, 8), 512), ((8, 8, 8, 2), 1024), ((8, 8, 8, 3, 3), 4608)])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_rotate_weight_workspace_whole_panels(su, du, io):
