@@ -179,7 +179,7 @@ __device__ __forceinline__ void col_store(__amdgpu_buffer_rsrc_t r, int vo, int 
 // every kDenseWaves-th chunk of the share.  Columns past ncols re-read the
 // last column (pair) and are not stored.
 template <int NQ, int CPL, typename TIN, typename TOUT>
-__global__ void __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(NQ == 8 || CPL == 2 ? 3 : 4)))
+__global__ void __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(NQ == 8 || (CPL == 2 && NQ == 7) ? 3 : 4)))
 col_dense_kernel(DenseParams p) {
   __shared__ __align__(16) float Mf[kDenseMaxRows * kDenseStride];
   __shared__ __align__(16) float Mt[kDenseMaxRows * kDenseStride];
@@ -188,7 +188,6 @@ col_dense_kernel(DenseParams p) {
   constexpr int KP = 4 * NQ;
   const int64_t rt = blockIdx.x / p.splits;
   const int split = blockIdx.x - (int)rt * p.splits;
-  compose(p, rt, Mf, Mt, cf);
   const int n = p.nsub;
   const int64_t pre = rt / p.suf, q = rt - pre * p.suf;
   const int64_t row_base = pre * n * p.suf + q;
@@ -201,13 +200,23 @@ col_dense_kernel(DenseParams p) {
   // bytes from one row of the group to the next (the host keeps nsub of them below 2^31)
   const int sx = (int)(p.suf * p.ldx * (int64_t)sizeof(TIN));
   const int sy = (int)(p.suf * p.ldy * (int64_t)sizeof(TOUT));
-  for (int64_t c = c_lo + wave; c < c_hi; c += kDenseWaves) {
-    const int64_t col = (c * 64 + lane) * CPL;
-    const bool valid = col < p.ncols;
-    const int vx = (int)((valid ? col : p.ncols - CPL) * (int64_t)sizeof(TIN));
-    W xw[KP];
+  // The chunk's column words: the next chunk's loads go out as soon as this
+  // chunk's products are issued (before its stores), the first chunk's before
+  // M is composed, so each wave has one chunk's loads in flight while it
+  // computes, stores or composes.
+  W xw[KP];
+  auto load = [&](int64_t cc) {
+    const int64_t col = (cc * 64 + lane) * CPL;
+    const int vx = (int)((col < p.ncols ? col : p.ncols - CPL) * (int64_t)sizeof(TIN));
 #pragma unroll
     for (int k = 0; k < KP; ++k) xw[k] = k < n ? buf_ld<W>(rx, vx, k * sx) : W{};
+  };
+  int64_t c = c_lo + wave;
+  if (c < c_hi) load(c);
+  compose(p, rt, Mf, Mt, cf);
+  for (; c < c_hi; c += kDenseWaves) {
+    const int64_t col = (c * 64 + lane) * CPL;
+    const bool valid = col < p.ncols;
     f32x4 acc[CPL][NQ];
 #pragma unroll
     for (int e = 0; e < CPL; ++e)
@@ -235,6 +244,8 @@ col_dense_kernel(DenseParams p) {
                                                            0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (c + kDenseWaves < c_hi) load(c + kDenseWaves);
+    __builtin_amdgcn_sched_barrier(0);
     if (valid) {
       const int vy = (int)(col * (int64_t)sizeof(TOUT));
 #pragma unroll
