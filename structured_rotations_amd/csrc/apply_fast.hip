@@ -574,7 +574,8 @@ __device__ __forceinline__ float ld_scale(const RowParams& p, int grp) {
 // o = min(4h + j, 4), and the two 2 x 2 blocks of columns o (h = 0, 1).
 // Inverse: c5[d4][h][k] = C5_{2g+d4}[k][o] and all five 2 x 2 blocks.
 // Forward bf16 and int8 coefficients stay as loaded (raw bits in the slots,
-// int8 group scales in slots 28..31) and decode_tail widens them where the
+// a bf16 radix-5 row as the three words covering it and its alignment, int8
+// group scales in slots 28..31) and decode_tail widens them where the
 // round uses them, so the load's wait does not land where it is issued; the
 // inverse widens at load (its slots are all taken).
 template <typename TB, bool TR>
@@ -599,9 +600,16 @@ __device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s
         d[0] = __uint_as_float(a.x); d[1] = __uint_as_float(a.y); d[2] = __uint_as_float(a.z); d[3] = __uint_as_float(a.w);
         d[4] = ld_coef1<TB>(rs, base + o * 5 + 4, soff5, sc);
       } else if constexpr (!TR && std::is_same<TB, uint16_t>::value) {
-#pragma unroll
-        for (int k = 0; k < 5; ++k)
-          d[k] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (base + o * 5 + k) * 2, soff5, 0));
+        // the row's 10 bytes start 2-byte aligned: one 4-byte and one 8-byte
+        // load from the 4-byte boundary below it cover them (2 bytes past the
+        // row lie in the radix-2 blocks stored after this stage); d[3] keeps
+        // the byte offset's bit 1 for decode_tail
+        const int a = soff5 + (base + o * 5) * 2;
+        const int a4 = a & ~3;
+        const uint32_t w0 = __builtin_amdgcn_raw_buffer_load_b32(rs, a4, 0, 0);
+        const u32x2 w12 = __builtin_amdgcn_raw_buffer_load_b64(rs, a4 + 4, 0, 0);
+        d[0] = __uint_as_float(w0); d[1] = __uint_as_float(w12.x); d[2] = __uint_as_float(w12.y);
+        d[3] = __uint_as_float((uint32_t)(a & 2));
       } else if constexpr (!TR) {
 #pragma unroll
         for (int k = 0; k < 5; ++k)
@@ -643,7 +651,19 @@ __device__ __forceinline__ void decode_tail(const Cbuf& raw, Cbuf& c) {
     for (int i = 0; i < 40; ++i) c.v[i] = raw.v[i];
   } else if constexpr (std::is_same<TB, uint16_t>::value) {
 #pragma unroll
-    for (int i = 0; i < 20; ++i) c.v[i] = __uint_as_float(__float_as_uint(raw.v[i]) << 16);
+    for (int r = 0; r < 4; ++r) {
+      // row r's five bf16 values from the 12 loaded bytes, 2 bytes in when the
+      // row started at bit 1 of the byte offset
+      const float* w = &raw.v[5 * r];
+      const uint32_t sh = __float_as_uint(w[3]) * 8u;
+      const uint32_t w0 = __float_as_uint(w[0]), w1 = __float_as_uint(w[1]), w2 = __float_as_uint(w[2]);
+      const uint32_t f0 = __builtin_amdgcn_alignbit(w1, w0, sh), f1 = __builtin_amdgcn_alignbit(w2, w1, sh);
+      c.v[5 * r] = bf16_lo(f0);
+      c.v[5 * r + 1] = bf16_hi(f0);
+      c.v[5 * r + 2] = bf16_lo(f1);
+      c.v[5 * r + 3] = bf16_hi(f1);
+      c.v[5 * r + 4] = bf16_lo(w2 >> sh);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t a = __float_as_uint(raw.v[20 + 4 * h]), b = __float_as_uint(raw.v[21 + 4 * h]);
