@@ -574,8 +574,8 @@ __device__ __forceinline__ float ld_scale(const RowParams& p, int grp) {
 // o = min(4h + j, 4), and the two 2 x 2 blocks of columns o (h = 0, 1).
 // Inverse: c5[d4][h][k] = C5_{2g+d4}[k][o] and all five 2 x 2 blocks.
 // Forward bf16 and int8 coefficients stay as loaded (raw bits in the slots,
-// a bf16 radix-5 row as the three words covering it and its alignment, int8
-// group scales in slots 28..31) and decode_tail widens them where the
+// a radix-5 row as the words covering it and its alignment, int8 group
+// scales in slots 28..31) and decode_tail widens them where the
 // round uses them, so the load's wait does not land where it is issued; the
 // inverse widens at load (its slots are all taken).
 template <typename TB, bool TR>
@@ -611,9 +611,13 @@ __device__ __forceinline__ void load_tail(const RowParams& p, const StageFast& s
         d[0] = __uint_as_float(w0); d[1] = __uint_as_float(w12.x); d[2] = __uint_as_float(w12.y);
         d[3] = __uint_as_float((uint32_t)(a & 2));
       } else if constexpr (!TR) {
-#pragma unroll
-        for (int k = 0; k < 5; ++k)
-          d[k] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, base + o * 5 + k, soff5, 0));
+        // the row's 5 bytes: one 8-byte load from the 4-byte boundary below
+        // them (up to 3 bytes past the row lie in the radix-2 blocks stored
+        // after this stage); d[2] keeps the byte offset's low two bits
+        const int a = soff5 + base + o * 5;
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs, a & ~3, 0, 0);
+        d[0] = __uint_as_float(w.x); d[1] = __uint_as_float(w.y);
+        d[2] = __uint_as_float((uint32_t)(a & 3));
         if (h == 0) c.v[28 + d4] = sc;
       } else {
 #pragma unroll
@@ -672,7 +676,17 @@ __device__ __forceinline__ void decode_tail(const Cbuf& raw, Cbuf& c) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 20; ++i) c.v[i] = (float)(int8_t)__float_as_uint(raw.v[i]) * raw.v[28 + i / 10];
+    for (int r = 0; r < 4; ++r) {
+      // row r's five codes from the 8 loaded bytes, starting at the byte
+      // offset's low two bits; scale of group d4 = r / 2
+      const float* w = &raw.v[5 * r];
+      const uint32_t sh = __float_as_uint(w[2]) * 8u;
+      const uint32_t f = __builtin_amdgcn_alignbit(__float_as_uint(w[1]), __float_as_uint(w[0]), sh);
+      const float sc = raw.v[28 + r / 2];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) c.v[5 * r + n] = (float)(int8_t)(f >> (8 * n)) * sc;
+      c.v[5 * r + 4] = (float)(int8_t)(__float_as_uint(w[1]) >> sh) * sc;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t a = __float_as_uint(raw.v[20 + 4 * h]);
