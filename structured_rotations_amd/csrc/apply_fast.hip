@@ -179,13 +179,14 @@ __device__ __forceinline__ void decode_coef(const float (&raw)[2][8], float (&cf
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     if constexpr (std::is_same<TB, int8_t>::value && !TR) {
-      // code c as the byte c + 128, then (c + 128) sc - 128 sc: c * sc rounded once
-      const float sc = raw[0][2], off = -128.0f * sc;
+      // c * sc rounded once; the signed byte converts in one instruction
+      // (sign-extending byte select)
+      const float sc = raw[0][2];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        const uint32_t u = __float_as_uint(raw[h][w]) ^ 0x80808080u;
+        const uint32_t u = __float_as_uint(raw[h][w]);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) cf[h][4 * w + n] = fmaf((float)((u >> (8 * n)) & 0xffu), sc, off);
+        for (int n = 0; n < 4; ++n) cf[h][4 * w + n] = (float)(int8_t)(u >> (8 * n)) * sc;
       }
     } else if constexpr (std::is_same<TB, uint16_t>::value && !TR && (B == 8 || B == 4)) {
 #pragma unroll
