@@ -117,8 +117,11 @@ __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& s
   const int soff = __builtin_amdgcn_readfirstlane((sd.blk_off + g0 * B * B) * SZ);
   if constexpr (std::is_same<TB, int8_t>::value) {
     static_assert(B == 8, "int8 rounds are radix 8");
-    const float sc = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(scale_rsrc(p), (sd.grp_off + g0 + gb) * 4, 0, 0));
+    // the round's part of the scale offset is uniform (scalar offset), the
+    // lane's part one register (per-round vector offsets would stay live
+    // across the unrolled tile and spill)
+    const int ssoff = __builtin_amdgcn_readfirstlane((sd.grp_off + g0) * 4);
+    const float sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scale_rsrc(p), gb * 4, ssoff, 0));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int o = 4 * h + j;
