@@ -734,46 +734,56 @@ __device__ __forceinline__ void tail_round(float* tile, int g, const Cbuf& craw,
         x[q][1][k] = G[1] * a + G[3] * b;
       }
   }
-  // D[i][jj] = x[row 4q + i][(k, d4)] * C5[4h + jj][k]
-  f32x4 acc[2][2][2];
+  // Outputs 0..3 on the matrix cores, D[i][jj] = x[row 4q + i][(k, d4)] * C5[jj][k]:
+  // lane j ends with output j for the four rows of its quad.
+  f32x4 acc[2][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int d4 = 0; d4 < 2; ++d4)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc[q][d4][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][d4][0], c.v[(d4 * 2 + h) * 5], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                           0, 0, 0);
+      acc[q][d4] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][d4][0], c.v[d4 * 10], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
   for (int k = 1; k < 5; ++k)
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int d4 = 0; d4 < 2; ++d4)
+        acc[q][d4] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][d4][k], c.v[d4 * 10 + k], acc[q][d4], 0, 0, 0);
+  // Output 4 on the vector ALU, for the lane's own row 4q + j (its h = 1
+  // slots hold coefficient row 4 in every lane): five FMAs per (q, d4)
+  // instead of a matrix-core chain of which one lane in four is used.
+  float y4[2][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[q][d4][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[q][d4][k], c.v[(d4 * 2 + h) * 5 + k], acc[q][d4][h], 0, 0, 0);
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int o = 4 * h + j;   // this lane's radix-5 output
-    if (o < 5) {
+    for (int d4 = 0; d4 < 2; ++d4) {
+      const float* c4 = &c.v[d4 * 10 + 5];
+      float t = c4[0] * x[q][d4][0];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        f32x4 z0 = acc[q][0][h], z1 = acc[q][1][h];
-        if constexpr (!TR) {
-          // forward: 2 x 2 block of column o on the pair (d4 = 0, 1)
-          const float* G = &c.v[20 + 4 * h];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = acc[q][0][h][i], b = acc[q][1][h][i];
-            z0[i] = G[0] * a + G[1] * b;
-            z1[i] = G[2] * a + G[3] * b;
-          }
-        }
-        *reinterpret_cast<f32x4*>(tile + 4 * Lay::unit(col0 + 2 * o) + PLANE * q) = z0;
-        *reinterpret_cast<f32x4*>(tile + 4 * Lay::unit(col0 + 2 * o + 1) + PLANE * q) = z1;
-      }
+      for (int k = 1; k < 5; ++k) t = fmaf(c4[k], x[q][d4][k], t);
+      y4[q][d4] = t;
     }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    f32x4 z0 = acc[q][0], z1 = acc[q][1];
+    float w0 = y4[q][0], w1 = y4[q][1];
+    if constexpr (!TR) {
+      // forward: the 2 x 2 block of column o on the pair (d4 = 0, 1)
+      const float* G = &c.v[20];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = acc[q][0][i], b = acc[q][1][i];
+        z0[i] = G[0] * a + G[1] * b;
+        z1[i] = G[2] * a + G[3] * b;
+      }
+      const float* G4 = &c.v[24];
+      w0 = G4[0] * y4[q][0] + G4[1] * y4[q][1];
+      w1 = G4[2] * y4[q][0] + G4[3] * y4[q][1];
+    }
+    *reinterpret_cast<f32x4*>(tile + 4 * Lay::unit(col0 + 2 * j) + PLANE * q) = z0;
+    *reinterpret_cast<f32x4*>(tile + 4 * Lay::unit(col0 + 2 * j + 1) + PLANE * q) = z1;
+    tile[4 * Lay::unit(col0 + 8) + j + PLANE * q] = w0;
+    tile[4 * Lay::unit(col0 + 9) + j + PLANE * q] = w1;
   }
 }
 
