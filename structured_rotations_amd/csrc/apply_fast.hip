@@ -312,18 +312,101 @@ __device__ __forceinline__ void read_inputs(const float* tile, int g, int j, flo
   }
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 as_s16x4(uint32_t w0, uint32_t w1) {
+  s16x4 r;
+  const uint32_t w[2] = {w0, w1};
+  __builtin_memcpy(&r, w, 8);
+  return r;
+}
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+  bf16x2_t r;
+  __builtin_memcpy(&r, &w, 4);
+  return r;
+}
+// x[0..3] = hi + lo + e with hi = bf16(x), lo = bf16(x - hi) (nearest even),
+// |e| <= 2^-16 |x|.  x - hi is exact in fp32 (hi is x rounded to 8 bits); it
+// comes out of one bf16 dot product, (-1, 0) . (hi_0, hi_1) + x_0, per value.
+__device__ __forceinline__ void split_bf16x4(const float* x, s16x4& hi, s16x4& lo) {
+  const uint32_t h0 = pack_bf16x2_hw(x[0], x[1]);
+  const uint32_t h1 = pack_bf16x2_hw(x[2], x[3]);
+  // (-1, 0) and (0, -1) go in scalar registers: as an inline constant the
+  // compiler writes (-1, 0) as "-1.0", which the dot product does not read
+  // as a bf16 pair (its results came out far off on the device)
+  uint32_t wl = 0x0000bf80u, wh = 0xbf800000u;
+  asm("" : "+s"(wl), "+s"(wh));
+  const bf16x2_t m_lo = as_bf16x2(wl), m_hi = as_bf16x2(wh);
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(h0), m_lo, x[0], false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(h0), m_hi, x[1], false);
+  const float r2 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(h1), m_lo, x[2], false);
+  const float r3 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(h1), m_hi, x[3], false);
+  hi = as_s16x4(h0, h1);
+  lo = as_s16x4(pack_bf16x2_hw(r0, r1), pack_bf16x2_hw(r2, r3));
+}
+// Rounds that take the split bf16 products: bf16 rows, bf16 blocks, forward.
+// (fp32 blocks split in the round as well, ch xh + ch xl + cl xh, measured
+// 10% slower than the fp32 products at d = 4096: the coefficient split adds
+// as many VALU instructions as the data split.)
+template <typename T, typename TB, bool TR>
+constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB, uint16_t>::value && !TR;
+
 // One round of products, ordered so that no LDS latency lands on the matrix
 // cores: the h = 0 outputs are written while the h = 1 chain runs, the next
 // round's inputs are read after those writes (so the next round waits only
 // for its own reads and the writes before them, never for the last writes),
 // and the h = 1 outputs go last.  Radix 8 only (two output halves).
-template <class Sch, int B, int S, bool DIRECT, bool NEXT, typename T, typename TB, bool TR>
+//
+// SPLIT (bf16 rows, bf16 blocks, forward): the products run as
+// v_mfma_f32_4x4x4_16b_bf16 (64 products per lane and instruction) instead of
+// 4x4x1 fp32 (16).  Each fp32 input is split into two bfloat16 values,
+// hi = bf16(x) and lo = bf16(x - hi), so |x - hi - lo| <= 2^-16 |x|; the
+// block rows are used as loaded.  Every product of two bf16 values is exact
+// in fp32 and the sums accumulate in fp32, so C x = C xh + C xl up to 2^-16
+// relative, far below the bf16 rounding of the output (fp32 rows keep the
+// fp32 products).  Lane j's A operand for k-chunk c is C[4h + j][4c .. 4c+3],
+// its B operand x[row][4c .. 4c + 3]: per round four chains of 4 products
+// instead of four chains of 8.  EXACT: the inputs are bf16 values (the first
+// stage of a forward transform of bf16 rows), lo = 0 and its products drop.
+template <class Sch, int B, int S, bool DIRECT, bool NEXT, typename T, typename TB, bool TR, bool SPLIT = false,
+          bool EXACT = false>
 __device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, int gn,
                                                const float (&craw)[2][8], const float (&xv)[2][8],
                                                float (&xn)[2][8], int64_t row0, int nr, int j) {
   static_assert(B == 8, "the pipelined round is written for radix 8");
+  static_assert(!SPLIT || (std::is_same<TB, uint16_t>::value && !TR), "split products take packed bf16 block rows");
+  // products per chain, and how many of the h = 1 chain run before the h = 0 writes
+  constexpr int PER = EXACT ? 1 : 2;
+  constexpr int NT = SPLIT ? 2 * PER : 8;
+  constexpr int NT1 = SPLIT ? PER : 2;
   float cf[2][8];
-  decode_coef<B, TB, TR>(craw, cf);
+  if constexpr (!SPLIT) decode_coef<B, TB, TR>(craw, cf);
+  s16x4 ch[2][2], xh[2][2], xl[2][2];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ch[h][c] = as_s16x4(__float_as_uint(craw[h][2 * c]), __float_as_uint(craw[h][2 * c + 1]));
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (EXACT)
+          xh[q][c] = as_s16x4(pack_bf16x2_hw(xv[q][4 * c], xv[q][4 * c + 1]), pack_bf16x2_hw(xv[q][4 * c + 2], xv[q][4 * c + 3]));
+        else
+          split_bf16x4(&xv[q][4 * c], xh[q][c], xl[q][c]);
+      }
+  }
+  // product t of the chain of output half h and row quad q
+  auto term = [&](int h, int q, int t, f32x4 acc) -> f32x4 {
+    if constexpr (!SPLIT) {
+      return __builtin_amdgcn_mfma_f32_4x4x1f32(cf[h][t], xv[q][t], acc, 0, 0, 0);
+    } else {
+      const int c = t / PER;
+      const s16x4 b = t % PER ? xl[q][c] : xh[q][c];
+      return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ch[h][c], b, acc, 0, 0, 0);
+    }
+  };
   using Lay = typename Sch::Lay;
   constexpr int PLANE = 4 * Lay::units(Sch::D);
   constexpr bool LIN = linear_stage<Lay, Sch::D, B, S>();
@@ -332,21 +415,20 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
   auto out_addr = [&](int o) {
     return LIN ? 4 * (Lay::unit(o * S) - Lay::unit(0)) : 4 * Lay::unit(col0 + o * S) - 4 * Lay::unit(col0);
   };
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[2][2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    acc[q][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[0][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  for (int q = 0; q < 2; ++q) acc[q][0] = term(0, q, 0, zero);
 #pragma unroll
-  for (int k = 1; k < B; ++k)
+  for (int t = 1; t < NT; ++t)
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      acc[q][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[0][k], xv[q][k], acc[q][0], 0, 0, 0);
+    for (int q = 0; q < 2; ++q) acc[q][0] = term(0, q, t, acc[q][0]);
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[1][0], xv[q][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  for (int q = 0; q < 2; ++q) acc[q][1] = term(1, q, 0, zero);
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[1][1], xv[q][1], acc[q][1], 0, 0, 0);
+  for (int t = 1; t < NT1; ++t)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[q][1] = term(1, q, t, acc[q][1]);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!DIRECT) {
 #pragma unroll
@@ -359,10 +441,9 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
   if constexpr (NEXT) read_inputs<Sch, B, S>(tile, gn, j, xn);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 2; k < B; ++k) {
+  for (int t = NT1; t < NT; ++t) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      acc[q][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[1][k], xv[q][k], acc[q][1], 0, 0, 0);
+    for (int q = 0; q < 2; ++q) acc[q][1] = term(1, q, t, acc[q][1]);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (!DIRECT) {
@@ -445,7 +526,7 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   load_coef<Sp::B, TB, TR>(p, p.st[tp], grp_round<Sp::S>((rp + rot) % Rp), lane_grp<Sp::S>(gA, gB), j,
                            cf[(N + 3) % 4]);
   __builtin_amdgcn_sched_barrier(0);
-  products_write<Sch, B, S, DIRECT, (r + 1 < R), T, TB, TR>(p, tile, grp_round<S>((r + rot) % R) + gl,
+  products_write<Sch, B, S, DIRECT, (r + 1 < R), T, TB, TR, kSplitRound<T, TB, TR>, t == 0>(p, tile, grp_round<S>((r + rot) % R) + gl,
                                                    grp_round<S>((r + 1 + rot) % R) + gl, cf[N % 4], xv[N % 2],
                                                    xv[(N + 1) % 2], row0, nr, j);
   __builtin_amdgcn_sched_barrier(0);
@@ -797,7 +878,7 @@ constexpr int k5Threads = 64 * (k5CW + k5IOW);
 // round's inputs while their own h = 1 chain runs (products_write); the
 // inverse keeps one round's inputs at a time (its element-wise coefficient
 // loads leave no registers for a second set).
-template <class Lay, int S, bool TR, typename TB, typename NextLoad>
+template <class Lay, int S, bool TR, typename TB, bool SPLIT, typename NextLoad>
 __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, const StageFast& sd, Cbuf& X, Cbuf& Y,
                                             int gb, int j, NextLoad next) {
   using Sch = Sched<5120, Lay, List<St<8, S>>>;
@@ -806,19 +887,19 @@ __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, con
     float xa[2][8], xb[2][8];
     read_inputs<Sch, 8, S>(tile, 0 * kGPR + gb, j, xa);
     load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 0 * kGPR + gb, 1 * kGPR + gb, as8(X), xa, xb,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 0 * kGPR + gb, 1 * kGPR + gb, as8(X), xa, xb,
                                                              0, 0, j);
     load_coef<8, TB, TR>(p, sd, 2 * kGPR, gb, j, as8(X));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 1 * kGPR + gb, 2 * kGPR + gb, as8(Y), xb, xa,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 1 * kGPR + gb, 2 * kGPR + gb, as8(Y), xb, xa,
                                                              0, 0, j);
     load_coef<8, TB, TR>(p, sd, 3 * kGPR, gb, j, as8(Y));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 2 * kGPR + gb, 3 * kGPR + gb, as8(X), xa, xb,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 2 * kGPR + gb, 3 * kGPR + gb, as8(X), xa, xb,
                                                              0, 0, j);
     load_coef<8, TB, TR>(p, sd, 4 * kGPR, gb, j, as8(X));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR>(p, tile, 3 * kGPR + gb, 4 * kGPR + gb, as8(Y), xb, xa,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 3 * kGPR + gb, 4 * kGPR + gb, as8(Y), xb, xa,
                                                              0, 0, j);
     next(Y);   // the next stage's round 0 goes to Y
-    products_write<Sch, 8, S, false, false, uint16_t, TB, TR>(p, tile, 4 * kGPR + gb, 4 * kGPR + gb, as8(X), xa, xb,
+    products_write<Sch, 8, S, false, false, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 4 * kGPR + gb, 4 * kGPR + gb, as8(X), xa, xb,
                                                               0, 0, j);
   } else {
     load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
@@ -887,22 +968,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     // would exhaust the registers)
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[0], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[0], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[1], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[1], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[3], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[3], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[4], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
@@ -911,22 +992,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     if (tix >= p.ntiles) break;
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[0], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[0], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[1], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[1], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB>(p, tile, p.st[3], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[3], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB>(p, tile, p.st[4], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[4], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
