@@ -458,6 +458,9 @@ def main() -> int:
     ap.add_argument("--fp32-intermediates", action="store_true",
                     help="two-sided workload: keep the passes' intermediates in an fp32 workspace")
     ap.add_argument("--mode", default="throughput", choices=["throughput", "latency", "materialize", "vjp"])
+    ap.add_argument("--inverse", action="store_true",
+                    help="row workloads: time harp_apply_inverse instead of harp_apply (no cpu_baseline and no "
+                         "counter record: both belong to the forward transform)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the apply path has no cross-GPU step (rows are independent; "
@@ -472,8 +475,8 @@ def main() -> int:
 
     import torch
     torch.cuda.set_device(0)
-    line = throughput(args.workload, args, with_cpu=not args.no_cpu_baseline)
-    if args.workload == DEFAULT_WORKLOAD and not args.copy_calibration and not args.single:
+    line = throughput(args.workload, args, with_cpu=not args.no_cpu_baseline and not args.inverse)
+    if args.workload == DEFAULT_WORKLOAD and not args.copy_calibration and not args.single and not args.inverse:
         # the headline metric names both row lengths: d = 5120 rides along as
         # a sub-record with the same timing, roofline and counter fields
         sub = throughput(SECOND_WORKLOAD, args, with_cpu=False)
@@ -557,8 +560,12 @@ def throughput(name: str, args, with_cpu: bool) -> dict:
         blocks, scales = api.harp_materialize_blocks(sch, d, th, gs, args.blk)
         sg = torch.from_numpy(w["signs"]).cuda()
 
-        def step():
-            api.harp_apply(sch, d, blocks, scales, sg, x, y)
+        if getattr(args, "inverse", False):
+            def step():
+                api.harp_apply_inverse(sch, d, blocks, scales, sg, x, y)
+        else:
+            def step():
+                api.harp_apply(sch, d, blocks, scales, sg, x, y)
         alg_bytes = rows * d * eb * 2
         alg_flops = 2 * rows * d * sum(sch)      # b_t FMAs per element per stage
         units = rows
@@ -608,14 +615,17 @@ def throughput(name: str, args, with_cpu: bool) -> dict:
     # round trip of the whole batch through the inverse (one more launch,
     # untimed); the oracle's own check of the output is in cpu_baseline
     roundtrip = None
+    inverse = wl.kind == "apply" and getattr(args, "inverse", False)
     if not args.copy_calibration and wl.kind == "apply":
-        xb = api.harp_apply_inverse(sch, d, blocks, scales, sg, y)
+        back = api.harp_apply if inverse else api.harp_apply_inverse
+        xb = back(sch, d, blocks, scales, sg, y)
         torch.cuda.synchronize()
         roundtrip = float(row_rel_l2(xb.float().cpu().numpy(), x.float().cpu().numpy()).max())
 
     unit = {"apply": "rows/s", "rht": "rows/s", "two_sided": "weights/s"}[wl.kind]
     # counter records are taken on each workload's default configuration
-    traffic = None if (args.copy_calibration or args.fp32_intermediates) else traffic_from_profile(name, args.blk)
+    traffic = None if (args.copy_calibration or args.fp32_intermediates or inverse) else \
+        traffic_from_profile(name, args.blk)
     line = {
         "metric": "HARP apply rows/s + achieved HBM GB/s (% of peak), d=4096/5120 bf16",
         "value": round(value, 1),
@@ -650,6 +660,8 @@ def throughput(name: str, args, with_cpu: bool) -> dict:
     }
     if not args.copy_calibration:
         line["copy_ceiling"] = copy_ceiling(x, y, stream, achieved)
+    if inverse:
+        line["config"]["direction"] = "inverse"
     if wl.kind == "two_sided":
         line["config"]["intermediates"] = "fp32 workspace" if args.fp32_intermediates else "bf16, in place"
     if with_cpu and not args.copy_calibration:

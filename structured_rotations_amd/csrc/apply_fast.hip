@@ -344,12 +344,12 @@ __device__ __forceinline__ void split_bf16x4(const float* x, s16x4& hi, s16x4& l
   hi = as_s16x4(h0, h1);
   lo = as_s16x4(pack_bf16x2_hw(r0, r1), pack_bf16x2_hw(r2, r3));
 }
-// Rounds that take the split bf16 products: bf16 rows, bf16 blocks, forward.
+// Rounds that take the split bf16 products: bf16 rows, bf16 blocks.
 // (fp32 blocks split in the round as well, ch xh + ch xl + cl xh, measured
 // 10% slower than the fp32 products at d = 4096: the coefficient split adds
 // as many VALU instructions as the data split.)
 template <typename T, typename TB, bool TR>
-constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB, uint16_t>::value && !TR;
+constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB, uint16_t>::value;
 
 // One round of products, ordered so that no LDS latency lands on the matrix
 // cores: the h = 0 outputs are written while the h = 1 chain runs, the next
@@ -357,7 +357,7 @@ constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB
 // for its own reads and the writes before them, never for the last writes),
 // and the h = 1 outputs go last.  Radix 8 only (two output halves).
 //
-// SPLIT (bf16 rows, bf16 blocks, forward): the products run as
+// SPLIT (bf16 rows, bf16 blocks): the products run as
 // v_mfma_f32_4x4x4_16b_bf16 (64 products per lane and instruction) instead of
 // 4x4x1 fp32 (16).  Each fp32 input is split into two bfloat16 values,
 // hi = bf16(x) and lo = bf16(x - hi), so |x - hi - lo| <= 2^-16 |x|; the
@@ -367,14 +367,15 @@ constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB
 // fp32 products).  Lane j's A operand for k-chunk c is C[4h + j][4c .. 4c+3],
 // its B operand x[row][4c .. 4c + 3]: per round four chains of 4 products
 // instead of four chains of 8.  EXACT: the inputs are bf16 values (the first
-// stage of a forward transform of bf16 rows), lo = 0 and its products drop.
+// stage of a transform of bf16 rows: the loaded rows, or their products with
+// the signs), lo = 0 and its products drop.
 template <class Sch, int B, int S, bool DIRECT, bool NEXT, typename T, typename TB, bool TR, bool SPLIT = false,
           bool EXACT = false>
 __device__ __forceinline__ void products_write(const RowParams& p, float* tile, int g, int gn,
                                                const float (&craw)[2][8], const float (&xv)[2][8],
                                                float (&xn)[2][8], int64_t row0, int nr, int j) {
   static_assert(B == 8, "the pipelined round is written for radix 8");
-  static_assert(!SPLIT || (std::is_same<TB, uint16_t>::value && !TR), "split products take packed bf16 block rows");
+  static_assert(!SPLIT || std::is_same<TB, uint16_t>::value, "split products take bf16 block rows");
   // products per chain, and how many of the h = 1 chain run before the h = 0 writes
   constexpr int PER = EXACT ? 1 : 2;
   constexpr int NT = SPLIT ? 2 * PER : 8;
@@ -386,7 +387,17 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) ch[h][c] = as_s16x4(__float_as_uint(craw[h][2 * c]), __float_as_uint(craw[h][2 * c + 1]));
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (TR) {
+          // transposed rows arrive one element per word, already widened:
+          // their upper halves are the bf16 bits
+          const uint32_t w[4] = {__float_as_uint(craw[h][4 * c]), __float_as_uint(craw[h][4 * c + 1]),
+                                 __float_as_uint(craw[h][4 * c + 2]), __float_as_uint(craw[h][4 * c + 3])};
+          ch[h][c] = as_s16x4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+        } else {
+          ch[h][c] = as_s16x4(__float_as_uint(craw[h][2 * c]), __float_as_uint(craw[h][2 * c + 1]));
+        }
+      }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -968,22 +979,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     // would exhaust the registers)
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[0], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[0], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[1], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[1], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[3], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[3], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[4], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[4], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
@@ -992,22 +1003,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     if (tix >= p.ntiles) break;
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[0], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[0], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[1], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[1], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[3], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[3], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[4], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[4], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
