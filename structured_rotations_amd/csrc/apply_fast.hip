@@ -348,8 +348,11 @@ __device__ __forceinline__ void split_bf16x4(const float* x, s16x4& hi, s16x4& l
 // (fp32 blocks split in the round as well, ch xh + ch xl + cl xh, measured
 // 10% slower than the fp32 products at d = 4096: the coefficient split adds
 // as many VALU instructions as the data split.)
+// int8 codes are integers of at most 8 bits, exact in bf16: their rounds take
+// the split products too (forward; the group scale multiplies the sums).
 template <typename T, typename TB, bool TR>
-constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB, uint16_t>::value;
+constexpr bool kSplitRound = std::is_same<T, uint16_t>::value &&
+                             (std::is_same<TB, uint16_t>::value || (std::is_same<TB, int8_t>::value && !TR));
 
 // One round of products, ordered so that no LDS latency lands on the matrix
 // cores: the h = 0 outputs are written while the h = 1 chain runs, the next
@@ -364,7 +367,8 @@ constexpr bool kSplitRound = std::is_same<T, uint16_t>::value && std::is_same<TB
 // block rows are used as loaded.  Every product of two bf16 values is exact
 // in fp32 and the sums accumulate in fp32, so C x = C xh + C xl up to 2^-16
 // relative, far below the bf16 rounding of the output (fp32 rows keep the
-// fp32 products).  Lane j's A operand for k-chunk c is C[4h + j][4c .. 4c+3],
+// fp32 products).  int8 codes enter the same way (exact in bf16) and the
+// group's scale multiplies each finished sum.  Lane j's A operand for k-chunk c is C[4h + j][4c .. 4c+3],
 // its B operand x[row][4c .. 4c + 3]: per round four chains of 4 products
 // instead of four chains of 8.  EXACT: the inputs are bf16 values (the first
 // stage of a transform of bf16 rows: the loaded rows, or their products with
@@ -375,7 +379,9 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
                                                const float (&craw)[2][8], const float (&xv)[2][8],
                                                float (&xn)[2][8], int64_t row0, int nr, int j) {
   static_assert(B == 8, "the pipelined round is written for radix 8");
-  static_assert(!SPLIT || std::is_same<TB, uint16_t>::value, "split products take bf16 block rows");
+  constexpr bool I8 = std::is_same<TB, int8_t>::value;
+  static_assert(!SPLIT || std::is_same<TB, uint16_t>::value || (I8 && !TR),
+                "split products take bf16 block rows or forward int8 codes");
   // products per chain, and how many of the h = 1 chain run before the h = 0 writes
   constexpr int PER = EXACT ? 1 : 2;
   constexpr int NT = SPLIT ? 2 * PER : 8;
@@ -388,7 +394,14 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if constexpr (TR) {
+        if constexpr (I8) {
+          // four codes per word: exact as bf16 (sign-extending byte conversion, then a pack)
+          const uint32_t w = __float_as_uint(craw[h][c]);
+          float f[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) f[n] = (float)(int8_t)(w >> (8 * n));
+          ch[h][c] = as_s16x4(pack_bf16x2_hw(f[0], f[1]), pack_bf16x2_hw(f[2], f[3]));
+        } else if constexpr (TR) {
           // transposed rows arrive one element per word, already widened:
           // their upper halves are the bf16 bits
           const uint32_t w[4] = {__float_as_uint(craw[h][4 * c]), __float_as_uint(craw[h][4 * c + 1]),
@@ -440,6 +453,11 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
   for (int t = 1; t < NT1; ++t)
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[q][1] = term(1, q, t, acc[q][1]);
+  if constexpr (SPLIT && I8) {
+    // the group's scale (an unused slot of the forward int8 layout), once per sum
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[q][0] *= craw[0][2];
+  }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!DIRECT) {
 #pragma unroll
@@ -456,6 +474,10 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[q][1] = term(1, q, t, acc[q][1]);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (SPLIT && I8) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[q][1] *= craw[0][2];
   }
   if constexpr (!DIRECT) {
 #pragma unroll
