@@ -106,8 +106,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const RowParams& p)
 // as they arrive, the int8 group scale beside them: decode_coef widens them
 // where the round uses them, so no wait for the load lands where it is
 // issued (bf16 blocks then move half the bytes of fp32 at no extra stall).
-// The inverse reads columns one element at a time and widens each at once
-// (deferring those measured slower).
+// The inverse reads fp32 blocks as row pieces that decode_coef transposes
+// across the quad, and bf16 or int8 columns one element at a time, widened
+// at once (deferring those measured slower).
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g0, int gb, int j,
                                           float (&cf)[2][8]) {
@@ -136,6 +137,20 @@ __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& s
       }
     }
     if constexpr (!TR) cf[0][2] = sc;   // an unused slot of the forward layout
+    return;
+  }
+  if constexpr (TR && B == 8 && std::is_same<TB, float>::value) {
+    // transposed rows without element loads: lane j reads row 4c + j of the
+    // block at columns 4h .. 4h + 3 (16 contiguous bytes) for each (h, c);
+    // decode_coef turns each 4 x 4 piece around across the lane's quad
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, (gb * 64 + (4 * c + j) * 8 + 4 * h) * 4, soff, 0);
+        cf[h][4 * c + 0] = __uint_as_float(a.x); cf[h][4 * c + 1] = __uint_as_float(a.y);
+        cf[h][4 * c + 2] = __uint_as_float(a.z); cf[h][4 * c + 3] = __uint_as_float(a.w);
+      }
     return;
   }
 #pragma unroll
@@ -175,10 +190,48 @@ __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& s
   }
 }
 
+// 4 x 4 transpose across the four lanes j of a block: on entry lane j holds
+// row j (r[c] = S[j][c]), on exit column j (r[i] = S[i][j]).  Lane bit 0 is
+// swapped with register bit 0, then lane bit 1 with register bit 1; each swap
+// sends one register per pair to the partner lane (quad permutation) and keeps
+// the other.
+__device__ __forceinline__ float quad_xor(float v, int ctrl_xor) {
+  const int x = __float_as_int(v);
+  return __int_as_float(ctrl_xor == 1 ? __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true)    // [1,0,3,2]
+                                      : __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+}
+__device__ __forceinline__ void quad_transpose4(float* r, int j) {
+  const bool b0 = j & 1, b1 = j & 2;
+#pragma unroll
+  for (int k1 = 0; k1 < 2; ++k1) {
+    const float v = quad_xor(b0 ? r[2 * k1] : r[2 * k1 + 1], 1);
+    r[2 * k1] = b0 ? v : r[2 * k1];
+    r[2 * k1 + 1] = b0 ? r[2 * k1 + 1] : v;
+  }
+#pragma unroll
+  for (int k0 = 0; k0 < 2; ++k0) {
+    const float v = quad_xor(b1 ? r[k0] : r[k0 + 2], 2);
+    r[k0] = b1 ? v : r[k0];
+    r[k0 + 2] = b1 ? r[k0 + 2] : v;
+  }
+}
+
 // The fp32 coefficients of a buffer filled by load_coef.
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void decode_coef(const float (&raw)[2][8], float (&cf)[2][8]) {
   constexpr int NH = B > 4 ? 2 : 1;
+  if constexpr (TR && B == 8 && std::is_same<TB, float>::value) {
+    const int j = threadIdx.x & 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cf[h][i] = raw[h][i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) quad_transpose4(&cf[h][4 * c], j);
+    return;
+  }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     if constexpr (std::is_same<TB, int8_t>::value && !TR) {
