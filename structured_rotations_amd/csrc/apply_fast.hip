@@ -106,9 +106,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const RowParams& p)
 // as they arrive, the int8 group scale beside them: decode_coef widens them
 // where the round uses them, so no wait for the load lands where it is
 // issued (bf16 blocks then move half the bytes of fp32 at no extra stall).
-// The inverse reads fp32 blocks as row pieces that decode_coef transposes
-// across the quad, and bf16 or int8 columns one element at a time, widened
-// at once (deferring those measured slower).
+// The inverse reads fp32 and bf16 blocks as row pieces that are transposed
+// across the quad where the round uses them, and int8 columns one element
+// at a time, widened at once (deferring those measured slower).
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g0, int gb, int j,
                                           float (&cf)[2][8]) {
@@ -137,6 +137,19 @@ __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& s
       }
     }
     if constexpr (!TR) cf[0][2] = sc;   // an unused slot of the forward layout
+    return;
+  }
+  if constexpr (TR && B == 8 && std::is_same<TB, uint16_t>::value) {
+    // the same for bf16 rows: 8 bytes per piece, kept as two packed words
+    // (columns 4h, 4h + 1 and 4h + 2, 4h + 3 of row 4c + j) in slots 2c, 2c + 1
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, (gb * 64 + (4 * c + j) * 8 + 4 * h) * 2, soff, 0);
+        cf[h][2 * c] = __uint_as_float(a.x);
+        cf[h][2 * c + 1] = __uint_as_float(a.y);
+      }
     return;
   }
   if constexpr (TR && B == 8 && std::is_same<TB, float>::value) {
@@ -216,10 +229,41 @@ __device__ __forceinline__ void quad_transpose4(float* r, int j) {
   }
 }
 
+// The same transpose for a 4 x 4 piece of bf16 values packed in two words per
+// lane (w0 = elements 0, 1; w1 = elements 2, 3): lane bit 0 against the half
+// within a word (the partner's word arrives whole, one byte permute keeps
+// the right halves), then lane bit 1 against the word.
+__device__ __forceinline__ void quad_transpose4_bf16(uint32_t& w0, uint32_t& w1, int j) {
+  const bool b0 = j & 1, b1 = j & 2;
+  // lane bit 0 clear: (own lo, partner lo); set: (partner hi, own hi)
+  const uint32_t sel = b0 ? 0x03020706u : 0x05040100u;
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0xB1, 0xF, 0xF, true);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0xB1, 0xF, 0xF, true);
+  w0 = __builtin_amdgcn_perm(r0, w0, sel);
+  w1 = __builtin_amdgcn_perm(r1, w1, sel);
+  const uint32_t snd = b1 ? w0 : w1;
+  const uint32_t v = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x4E, 0xF, 0xF, true);
+  w0 = b1 ? v : w0;
+  w1 = b1 ? w1 : v;
+}
+
 // The fp32 coefficients of a buffer filled by load_coef.
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void decode_coef(const float (&raw)[2][8], float (&cf)[2][8]) {
   constexpr int NH = B > 4 ? 2 : 1;
+  if constexpr (TR && B == 8 && std::is_same<TB, uint16_t>::value) {
+    const int j = threadIdx.x & 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint32_t w0 = __float_as_uint(raw[h][2 * c]), w1 = __float_as_uint(raw[h][2 * c + 1]);
+        quad_transpose4_bf16(w0, w1, j);
+        cf[h][4 * c + 0] = bf16_lo(w0); cf[h][4 * c + 1] = bf16_hi(w0);
+        cf[h][4 * c + 2] = bf16_lo(w1); cf[h][4 * c + 3] = bf16_hi(w1);
+      }
+    return;
+  }
   if constexpr (TR && B == 8 && std::is_same<TB, float>::value) {
     const int j = threadIdx.x & 3;
 #pragma unroll
@@ -455,11 +499,10 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
           for (int n = 0; n < 4; ++n) f[n] = (float)(int8_t)(w >> (8 * n));
           ch[h][c] = as_s16x4(pack_bf16x2_hw(f[0], f[1]), pack_bf16x2_hw(f[2], f[3]));
         } else if constexpr (TR) {
-          // transposed rows arrive one element per word, already widened:
-          // their upper halves are the bf16 bits
-          const uint32_t w[4] = {__float_as_uint(craw[h][4 * c]), __float_as_uint(craw[h][4 * c + 1]),
-                                 __float_as_uint(craw[h][4 * c + 2]), __float_as_uint(craw[h][4 * c + 3])};
-          ch[h][c] = as_s16x4(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+          // row pieces of the block turned into column pieces across the quad
+          uint32_t w0 = __float_as_uint(craw[h][2 * c]), w1 = __float_as_uint(craw[h][2 * c + 1]);
+          quad_transpose4_bf16(w0, w1, threadIdx.x & 3);
+          ch[h][c] = as_s16x4(w0, w1);
         } else {
           ch[h][c] = as_s16x4(__float_as_uint(craw[h][2 * c]), __float_as_uint(craw[h][2 * c + 1]));
         }
