@@ -131,12 +131,14 @@ __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& s
         cf[h][0] = __uint_as_float(a.x);
         cf[h][1] = __uint_as_float(a.y);
       } else {
+        // inverse: the codes of row 4c + j at columns 4h .. 4h + 3 (one word
+        // per piece), transposed across the quad in decode_coef
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          cf[h][k] = (float)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, gb * 64 + o + k * 8, soff, 0) * sc;
+        for (int c = 0; c < 2; ++c)
+          cf[h][c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, gb * 64 + (4 * c + j) * 8 + 4 * h, soff, 0));
       }
     }
-    if constexpr (!TR) cf[0][2] = sc;   // an unused slot of the forward layout
+    cf[0][2] = sc;   // an unused slot of both layouts
     return;
   }
   if constexpr (TR && B == 8 && std::is_same<TB, uint16_t>::value) {
@@ -247,10 +249,37 @@ __device__ __forceinline__ void quad_transpose4_bf16(uint32_t& w0, uint32_t& w1,
   w1 = b1 ? w1 : v;
 }
 
+// The same for a 4 x 4 piece of bytes in one word per lane: lane bit 0
+// against byte bit 0, then lane bit 1 against byte bit 1, each one quad
+// permutation and one byte permute.
+__device__ __forceinline__ uint32_t quad_transpose4_i8(uint32_t w, int j) {
+  const bool b0 = j & 1, b1 = j & 2;
+  uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0xB1, 0xF, 0xF, true);
+  // lane bit 0 clear: (own 0, partner 0, own 2, partner 2); set: (partner 1, own 1, partner 3, own 3)
+  w = __builtin_amdgcn_perm(r, w, b0 ? 0x03070105u : 0x06020400u);
+  r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x4E, 0xF, 0xF, true);
+  // lane bit 1 clear: (own 0, own 1, partner 0, partner 1); set: (partner 2, partner 3, own 2, own 3)
+  return __builtin_amdgcn_perm(r, w, b1 ? 0x03020706u : 0x05040100u);
+}
+
 // The fp32 coefficients of a buffer filled by load_coef.
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void decode_coef(const float (&raw)[2][8], float (&cf)[2][8]) {
   constexpr int NH = B > 4 ? 2 : 1;
+  if constexpr (TR && std::is_same<TB, int8_t>::value) {
+    // code * scale rounded once, as in the forward decode
+    const int j = threadIdx.x & 3;
+    const float sc = raw[0][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t w = quad_transpose4_i8(__float_as_uint(raw[h][c]), j);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) cf[h][4 * c + n] = (float)(int8_t)(w >> (8 * n)) * sc;
+      }
+    return;
+  }
   if constexpr (TR && B == 8 && std::is_same<TB, uint16_t>::value) {
     const int j = threadIdx.x & 3;
 #pragma unroll
