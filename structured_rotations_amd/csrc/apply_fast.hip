@@ -1032,16 +1032,18 @@ constexpr int k5Threads = 64 * (k5CW + k5IOW);
 
 // One radix-8 stage of the 5120 kernel (5 rounds, stride S, stage params sd),
 // coefficient buffers alternating; on exit the next stage's first round is in
-// the buffer given by the round parity.  Forward rounds read the next
-// round's inputs while their own h = 1 chain runs (products_write); the
-// inverse keeps one round's inputs at a time (its element-wise coefficient
-// loads leave no registers for a second set).
+// the buffer given by the round parity.  Rounds read the next round's inputs
+// while their own h = 1 chain runs (products_write), except the inverse with
+// bf16 blocks, which keeps one round's inputs at a time.
 template <class Lay, int S, bool TR, typename TB, bool SPLIT, typename NextLoad>
 __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, const StageFast& sd, Cbuf& X, Cbuf& Y,
                                             int gb, int j, NextLoad next) {
   using Sch = Sched<5120, Lay, List<St<8, S>>>;
   // rounds 0..4: X holds round 0
-  if constexpr (!TR) {
+  // (inverse rounds of fp32 and int8 blocks read row pieces now, and have the
+  // registers for a second set of inputs: 0.367 -> 0.349 ms and 0.357 ->
+  // 0.349 ms; with bf16 blocks the second set measured 0.319 -> 0.334 ms)
+  if constexpr (!TR || !std::is_same<TB, uint16_t>::value) {
     float xa[2][8], xb[2][8];
     read_inputs<Sch, 8, S>(tile, 0 * kGPR + gb, j, xa);
     load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
