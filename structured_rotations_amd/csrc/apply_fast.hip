@@ -670,15 +670,6 @@ __device__ __forceinline__ void pipe_round(const RowParams& p, float* tile, floa
   constexpr int rp = NP - rounds_before_rt<Sch>(tp);
   using Sp = typename At<tp, typename Sch::L>::type;
   constexpr int Rp = Sch::D / Sp::B / kGPR;
-  if constexpr (TR && !std::is_same<TB, int8_t>::value) {
-    // the inverse's element-wise coefficient loads leave few registers: keep
-    // the lane's group indices opaque per round so the rounds' LDS addresses
-    // are recomputed where used instead of being hoisted and spilled (whose
-    // reloads wait for every load in flight): fp32 blocks 0.151 -> 0.146 ms,
-    // bf16 0.171 -> 0.153 ms; int8 measured 0.133 -> 0.140 ms and keeps the
-    // compiler's choice
-    asm volatile("" : "+v"(gA), "+v"(gB));
-  }
   const int gl = lane_grp<S>(gA, gB);
   __builtin_amdgcn_sched_barrier(0);
   load_coef<Sp::B, TB, TR>(p, p.st[tp], grp_round<Sp::S>((rp + rot) % Rp), lane_grp<Sp::S>(gA, gB), j,
