@@ -478,7 +478,7 @@ __device__ __forceinline__ void split_bf16x4(const float* x, s16x4& hi, s16x4& l
 // the split products too (forward; the group scale multiplies the sums).
 template <typename T, typename TB, bool TR>
 constexpr bool kSplitRound = std::is_same<T, uint16_t>::value &&
-                             (std::is_same<TB, uint16_t>::value || (std::is_same<TB, int8_t>::value && !TR));
+                             (std::is_same<TB, uint16_t>::value || std::is_same<TB, int8_t>::value);
 
 // One round of products, ordered so that no LDS latency lands on the matrix
 // cores: the h = 0 outputs are written while the h = 1 chain runs, the next
@@ -506,8 +506,7 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
                                                float (&xn)[2][8], int64_t row0, int nr, int j) {
   static_assert(B == 8, "the pipelined round is written for radix 8");
   constexpr bool I8 = std::is_same<TB, int8_t>::value;
-  static_assert(!SPLIT || std::is_same<TB, uint16_t>::value || (I8 && !TR),
-                "split products take bf16 block rows or forward int8 codes");
+  static_assert(!SPLIT || std::is_same<TB, uint16_t>::value || I8, "split products take bf16 or int8 blocks");
   // products per chain, and how many of the h = 1 chain run before the h = 0 writes
   constexpr int PER = EXACT ? 1 : 2;
   constexpr int NT = SPLIT ? 2 * PER : 8;
@@ -521,8 +520,10 @@ __device__ __forceinline__ void products_write(const RowParams& p, float* tile, 
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         if constexpr (I8) {
-          // four codes per word: exact as bf16 (sign-extending byte conversion, then a pack)
-          const uint32_t w = __float_as_uint(craw[h][c]);
+          // four codes per word: exact as bf16 (sign-extending byte conversion,
+          // then a pack); the inverse's row pieces are transposed across the quad first
+          uint32_t w = __float_as_uint(craw[h][c]);
+          if constexpr (TR) w = quad_transpose4_i8(w, threadIdx.x & 3);
           float f[4];
 #pragma unroll
           for (int n = 0; n < 4; ++n) f[n] = (float)(int8_t)(w >> (8 * n));
@@ -1038,19 +1039,19 @@ __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, con
     float xa[2][8], xb[2][8];
     read_inputs<Sch, 8, S>(tile, 0 * kGPR + gb, j, xa);
     load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 0 * kGPR + gb, 1 * kGPR + gb, as8(X), xa, xb,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && !TR && S == 640>(p, tile, 0 * kGPR + gb, 1 * kGPR + gb, as8(X), xa, xb,
                                                              0, 0, j);
     load_coef<8, TB, TR>(p, sd, 2 * kGPR, gb, j, as8(X));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 1 * kGPR + gb, 2 * kGPR + gb, as8(Y), xb, xa,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && !TR && S == 640>(p, tile, 1 * kGPR + gb, 2 * kGPR + gb, as8(Y), xb, xa,
                                                              0, 0, j);
     load_coef<8, TB, TR>(p, sd, 3 * kGPR, gb, j, as8(Y));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 2 * kGPR + gb, 3 * kGPR + gb, as8(X), xa, xb,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && !TR && S == 640>(p, tile, 2 * kGPR + gb, 3 * kGPR + gb, as8(X), xa, xb,
                                                              0, 0, j);
     load_coef<8, TB, TR>(p, sd, 4 * kGPR, gb, j, as8(X));
-    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 3 * kGPR + gb, 4 * kGPR + gb, as8(Y), xb, xa,
+    products_write<Sch, 8, S, false, true, uint16_t, TB, TR, SPLIT, SPLIT && !TR && S == 640>(p, tile, 3 * kGPR + gb, 4 * kGPR + gb, as8(Y), xb, xa,
                                                              0, 0, j);
     next(Y);   // the next stage's round 0 goes to Y
-    products_write<Sch, 8, S, false, false, uint16_t, TB, TR, SPLIT, SPLIT && S == 640>(p, tile, 4 * kGPR + gb, 4 * kGPR + gb, as8(X), xa, xb,
+    products_write<Sch, 8, S, false, false, uint16_t, TB, TR, SPLIT, SPLIT && !TR && S == 640>(p, tile, 4 * kGPR + gb, 4 * kGPR + gb, as8(X), xa, xb,
                                                               0, 0, j);
   } else {
     load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
@@ -1119,22 +1120,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     // would exhaust the registers)
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[0], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[0], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[1], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[1], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[3], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[3], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[4], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[4], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
@@ -1143,22 +1144,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     if (tix >= p.ntiles) break;
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[0], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[0], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[1], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[1], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[3], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[3], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && !TR>(p, tile, p.st[4], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[4], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
