@@ -1025,8 +1025,8 @@ constexpr int k5Threads = 64 * (k5CW + k5IOW);
 // One radix-8 stage of the 5120 kernel (5 rounds, stride S, stage params sd),
 // coefficient buffers alternating; on exit the next stage's first round is in
 // the buffer given by the round parity.  Rounds read the next round's inputs
-// while their own h = 1 chain runs (products_write), except the inverse with
-// bf16 blocks, which keeps one round's inputs at a time.
+// while their own h = 1 chain runs (products_write), except the inverse of
+// fp32 rows with bf16 blocks, which keeps one round's inputs at a time.
 template <class Lay, int S, bool TR, typename TB, bool SPLIT, typename NextLoad>
 __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, const StageFast& sd, Cbuf& X, Cbuf& Y,
                                             int gb, int j, NextLoad next) {
@@ -1034,8 +1034,9 @@ __device__ __forceinline__ void stage8_5120(const RowParams& p, float* tile, con
   // rounds 0..4: X holds round 0
   // (inverse rounds of fp32 and int8 blocks read row pieces now, and have the
   // registers for a second set of inputs: 0.367 -> 0.349 ms and 0.357 ->
-  // 0.349 ms; with bf16 blocks the second set measured 0.319 -> 0.334 ms)
-  if constexpr (!TR || !std::is_same<TB, uint16_t>::value) {
+  // 0.349 ms; with bf16 blocks the second set measured 0.319 -> 0.334 ms on
+  // fp32 products, 0.323 -> 0.302 ms on the split bf16 products)
+  if constexpr (!TR || !std::is_same<TB, uint16_t>::value || SPLIT) {
     float xa[2][8], xb[2][8];
     read_inputs<Sch, 8, S>(tile, 0 * kGPR + gb, j, xa);
     load_coef<8, TB, TR>(p, sd, 1 * kGPR, gb, j, as8(Y));
@@ -1120,22 +1121,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     // would exhaust the registers)
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[0], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[0], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[1], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[1], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], ca, cb, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[3], cb, ca, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[3], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[4], ca, cb, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[4], ca, cb, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
@@ -1144,22 +1145,22 @@ __global__ void __launch_bounds__(k5Threads) apply_5120_kernel(RowParams p) {
     if (tix >= p.ntiles) break;
     asm volatile("" : "+v"(gb), "+v"(j));
     if constexpr (!TR) {
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[0], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[0], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[1], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[1], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[1], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[3], p.st[4], 0, gb, j, d); });
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[3], p.st[4], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[0], 0, gb, j, as8(d)); });
     } else {
       stage_tail_5120<Lay, TR, TB>(p, tile, p.st[1], p.st[0], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[2], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[2], cb, ca, gb, j,
+      stage8_5120<Lay, 10, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[2], cb, ca, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[3], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[3], ca, cb, gb, j,
+      stage8_5120<Lay, 80, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[3], ca, cb, gb, j,
                                    [&](Cbuf& d) { load_coef<8, TB, TR>(p, p.st[4], 0, gb, j, as8(d)); });
-      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR> && (!TR || std::is_same<TB, int8_t>::value)>(p, tile, p.st[4], cb, ca, gb, j,
+      stage8_5120<Lay, 640, TR, TB, kSplitRound<T, TB, TR>>(p, tile, p.st[4], cb, ca, gb, j,
                                     [&](Cbuf& d) { load_tail<TB, TR>(p, p.st[1], p.st[0], 0, gb, j, d); });
     }
     if constexpr (!std::is_same<T, float>::value) compute_copy_out<T, Lay, 64 * k5CW, 2>(p, tile, tix, threadIdx.x);
