@@ -106,9 +106,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const RowParams& p)
 // as they arrive, the int8 group scale beside them: decode_coef widens them
 // where the round uses them, so no wait for the load lands where it is
 // issued (bf16 blocks then move half the bytes of fp32 at no extra stall).
-// The inverse reads fp32 and bf16 blocks as row pieces that are transposed
-// across the quad where the round uses them, and int8 columns one element
-// at a time, widened at once (deferring those measured slower).
+// The inverse of a radix-8 stage reads block rows as 16-, 8- or 4-byte
+// pieces (fp32, bf16, int8) that are transposed across the quad where the
+// round uses them; other radices read columns one element at a time.
 template <int B, typename TB, bool TR>
 __device__ __forceinline__ void load_coef(const RowParams& p, const StageFast& sd, int g0, int gb, int j,
                                           float (&cf)[2][8]) {
@@ -486,15 +486,16 @@ constexpr bool kSplitRound = std::is_same<T, uint16_t>::value &&
 // for its own reads and the writes before them, never for the last writes),
 // and the h = 1 outputs go last.  Radix 8 only (two output halves).
 //
-// SPLIT (bf16 rows, bf16 blocks): the products run as
+// SPLIT (bf16 rows with bf16 or int8 blocks): the products run as
 // v_mfma_f32_4x4x4_16b_bf16 (64 products per lane and instruction) instead of
 // 4x4x1 fp32 (16).  Each fp32 input is split into two bfloat16 values,
-// hi = bf16(x) and lo = bf16(x - hi), so |x - hi - lo| <= 2^-16 |x|; the
-// block rows are used as loaded.  Every product of two bf16 values is exact
-// in fp32 and the sums accumulate in fp32, so C x = C xh + C xl up to 2^-16
-// relative, far below the bf16 rounding of the output (fp32 rows keep the
-// fp32 products).  int8 codes enter the same way (exact in bf16) and the
-// group's scale multiplies each finished sum.  Lane j's A operand for k-chunk c is C[4h + j][4c .. 4c+3],
+// hi = bf16(x) and lo = bf16(x - hi), so |x - hi - lo| <= 2^-16 |x|; bf16
+// block rows are used as loaded (inverse: transposed across the quad).
+// Every product of two bf16 values is exact in fp32 and the sums accumulate
+// in fp32, so C x = C xh + C xl up to 2^-16 relative, far below the bf16
+// rounding of the output (fp32 rows keep the fp32 products).  int8 codes
+// enter the same way (exact in bf16) and the group's scale multiplies each
+// finished sum.  Lane j's A operand for k-chunk c is C[4h + j][4c .. 4c + 3],
 // its B operand x[row][4c .. 4c + 3]: per round four chains of 4 products
 // instead of four chains of 8.  EXACT: the inputs are bf16 values (the first
 // stage of a transform of bf16 rows: the loaded rows, or their products with
